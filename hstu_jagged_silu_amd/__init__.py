@@ -1,0 +1,353 @@
+"""HSTU jagged SiLU attention on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libhstu.so`` (C ABI in ``include/hstu.h``). Every
+function here only marshals arguments: it checks tensor placement, dtypes and
+shapes, allocates the output and workspace through PyTorch, and calls the
+library on the current HIP stream. All arithmetic runs in the library's HIP
+kernels. If the library is missing, importing this package raises.
+
+Functions mirror the C entry points by name:
+
+* ``hstu_attn_fwd``        full causal path over jagged sequences
+* ``hstu_kv_append``       paged KV append
+* ``hstu_attn_fwd_cached`` new tokens against a cached, paged prefix
+* ``hstu_mfalcon_fwd``     M-FALCON candidate scoring
+* ``hstu_workspace_size``  workspace bytes of one call
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhstu.so")
+
+HSTU_F32, HSTU_BF16 = 0, 1
+HSTU_FN_FULL, HSTU_FN_CACHED, HSTU_FN_MFALCON = 0, 1, 2
+PAGE_SIZE = 64
+
+EXPORTED_SYMBOLS = (
+    "hstu_status_string", "hstu_version", "hstu_workspace_size", "hstu_attn_fwd",
+    "hstu_kv_append", "hstu_attn_fwd_cached", "hstu_mfalcon_fwd",
+)
+
+
+class HstuError(RuntimeError):
+    pass
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("alpha", ctypes.c_float), ("norm_n", ctypes.c_int32),
+        ("pos_tab", ctypes.c_void_p), ("n_pos", ctypes.c_int32), ("pos_head_stride", ctypes.c_int32),
+        ("time_tab", ctypes.c_void_p), ("n_time", ctypes.c_int32), ("time_head_stride", ctypes.c_int32),
+        ("ln_w", ctypes.c_void_p), ("ln_b", ctypes.c_void_p), ("ln_eps", ctypes.c_float),
+        ("timing_events", ctypes.c_void_p * 2),
+    ]
+
+
+class _KVCache(ctypes.Structure):
+    _fields_ = [
+        ("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p), ("ts_pages", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p), ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+                          "or `python hstu_jagged_silu_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(_Params)
+    K = ctypes.POINTER(_KVCache)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.hstu_status_string.restype = ctypes.c_char_p
+    lib.hstu_status_string.argtypes = [ctypes.c_int]
+    lib.hstu_version.restype = i32
+    lib.hstu_version.argtypes = []
+    lib.hstu_workspace_size.restype = sz
+    lib.hstu_workspace_size.argtypes = [i32, P, i32, i64, i32]
+    lib.hstu_attn_fwd.restype = ctypes.c_int
+    lib.hstu_attn_fwd.argtypes = [P, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hstu_kv_append.restype = ctypes.c_int
+    lib.hstu_kv_append.argtypes = [K, P, i32, vp, vp, i64, vp, vp, vp, vp]
+    lib.hstu_attn_fwd_cached.restype = ctypes.c_int
+    lib.hstu_attn_fwd_cached.argtypes = [P, i32, vp, vp, i32, i32, i64, vp, vp, vp, K, vp, vp, sz, vp]
+    lib.hstu_mfalcon_fwd.restype = ctypes.c_int
+    lib.hstu_mfalcon_fwd.argtypes = [P, i32, vp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    """The loaded ctypes library handle."""
+    return _lib
+
+
+def version() -> int:
+    return int(_lib.hstu_version())
+
+
+def status_string(code: int) -> str:
+    return _lib.hstu_status_string(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise HstuError(f"{what}: {status_string(code)}")
+
+
+# ---------------------------------------------------------------------------
+# argument marshalling
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LayerParams:
+    """Layer parameters (C struct hstu_params_t). Tables are fp32 device tensors,
+    shape [n] (shared by all heads) or [H, n] (one per head)."""
+    num_heads: int
+    head_dim: int
+    dtype: torch.dtype = torch.bfloat16
+    alpha: float = 1.0
+    norm_n: int = 0
+    pos_tab: Optional[torch.Tensor] = None
+    time_tab: Optional[torch.Tensor] = None
+    ln_w: Optional[torch.Tensor] = None
+    ln_b: Optional[torch.Tensor] = None
+    ln_eps: float = 1e-5
+
+    def c_struct(self, timing_events=None) -> _Params:
+        p = _Params()
+        p.num_heads = self.num_heads
+        p.head_dim = self.head_dim
+        p.dtype = {torch.bfloat16: HSTU_BF16, torch.float32: HSTU_F32}.get(self.dtype, -1)
+        p.alpha = self.alpha
+        p.norm_n = self.norm_n
+        for name in ("pos_tab", "time_tab"):
+            t = getattr(self, name)
+            n_field = "n_pos" if name == "pos_tab" else "n_time"
+            s_field = "pos_head_stride" if name == "pos_tab" else "time_head_stride"
+            if t is None:
+                setattr(p, name, None)
+                setattr(p, n_field, 0)
+                setattr(p, s_field, 0)
+                continue
+            _device_tensor(t, torch.float32, name)
+            if t.dim() == 1:
+                setattr(p, n_field, t.shape[0])
+                setattr(p, s_field, 0)
+            elif t.dim() == 2 and t.shape[0] == self.num_heads:
+                setattr(p, n_field, t.shape[1])
+                setattr(p, s_field, t.stride(0))
+            else:
+                raise ValueError(f"{name} must be [n] or [H, n]")
+            setattr(p, name, t.data_ptr())
+        for name in ("ln_w", "ln_b"):
+            t = getattr(self, name)
+            if t is not None:
+                _device_tensor(t, torch.float32, name)
+                if t.numel() != self.num_heads * self.head_dim:
+                    raise ValueError(f"{name} must have H*d elements")
+            setattr(p, name, None if t is None else t.data_ptr())
+        p.ln_eps = self.ln_eps
+        if timing_events is not None:
+            p.timing_events[0] = timing_events[0].cuda_event
+            p.timing_events[1] = timing_events[1].cuda_event
+        return p
+
+
+def _device_tensor(t, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def hstu_workspace_size(fn: int, params: LayerParams, batch: int, total_q_tokens: int, max_len: int) -> int:
+    """Workspace bytes for one call of entry point ``fn`` (HSTU_FN_*)."""
+    p = params.c_struct()
+    n = int(_lib.hstu_workspace_size(fn, ctypes.byref(p), batch, total_q_tokens, max_len))
+    if n == 0:
+        raise HstuError("hstu_workspace_size: invalid arguments")
+    return n
+
+
+def _workspace(ws, nbytes, device):
+    if ws is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _device_tensor(ws, torch.uint8, "workspace")
+    if ws.numel() < nbytes:
+        raise HstuError(f"workspace has {ws.numel()} bytes, {nbytes} needed")
+    return ws
+
+
+def _jagged_checks(params, q, k, v, u, ts, seq_offsets):
+    H, d = params.num_heads, params.head_dim
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _device_tensor(t, params.dtype, name)
+        if t.dim() != 3 or t.shape[1:] != (H, d):
+            raise ValueError(f"{name} must be [T, {H}, {d}]")
+    _device_tensor(u, params.dtype, "u")
+    if u.shape != (q.shape[0], H * d):
+        raise ValueError(f"u must be [T, {H * d}]")
+    _device_tensor(ts, torch.int64, "ts")
+    _device_tensor(seq_offsets, torch.int32, "seq_offsets")
+    if ts.shape != (q.shape[0],):
+        raise ValueError("ts must be [T]")
+
+
+def hstu_attn_fwd(q, k, v, u, ts, seq_offsets, max_len: int, params: LayerParams, *, y=None,
+                  workspace=None, timing_events=None):
+    """Full causal path. q, k, v: [T, H, d]; u: [T, H*d]; ts int64 [T];
+    seq_offsets int32 [B+1] on the GPU. Returns y [T, H*d]."""
+    _jagged_checks(params, q, k, v, u, ts, seq_offsets)
+    T, B = q.shape[0], seq_offsets.shape[0] - 1
+    y = torch.empty_like(u) if y is None else y
+    _device_tensor(y, params.dtype, "y")
+    nbytes = hstu_workspace_size(HSTU_FN_FULL, params, B, T, max_len)
+    ws = _workspace(workspace, nbytes, q.device)
+    p = params.c_struct(timing_events)
+    _check(_lib.hstu_attn_fwd(ctypes.byref(p), B, seq_offsets.data_ptr(), max_len, T, q.data_ptr(), k.data_ptr(),
+                              v.data_ptr(), u.data_ptr(), ts.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(),
+                              _stream()), "hstu_attn_fwd")
+    return y
+
+
+def hstu_mfalcon_fwd(q, k, v, u, ts, seq_offsets, num_candidates, max_len: int, params: LayerParams, *, y=None,
+                     workspace=None, timing_events=None):
+    """M-FALCON: each user's rows are [history | candidates]; num_candidates int32 [B]."""
+    _jagged_checks(params, q, k, v, u, ts, seq_offsets)
+    _device_tensor(num_candidates, torch.int32, "num_candidates")
+    T, B = q.shape[0], seq_offsets.shape[0] - 1
+    y = torch.empty_like(u) if y is None else y
+    _device_tensor(y, params.dtype, "y")
+    nbytes = hstu_workspace_size(HSTU_FN_MFALCON, params, B, T, max_len)
+    ws = _workspace(workspace, nbytes, q.device)
+    p = params.c_struct(timing_events)
+    _check(_lib.hstu_mfalcon_fwd(ctypes.byref(p), B, seq_offsets.data_ptr(), num_candidates.data_ptr(), max_len, T,
+                                 q.data_ptr(), k.data_ptr(), v.data_ptr(), u.data_ptr(), ts.data_ptr(),
+                                 y.data_ptr(), ws.data_ptr(), ws.numel(), _stream()), "hstu_mfalcon_fwd")
+    return y
+
+
+@dataclasses.dataclass
+class PagedKVCache:
+    """Caller-owned paged KV cache (C struct hstu_kv_cache_t).
+
+    k_pages, v_pages: [num_pages, H, 64, d]; ts_pages: int64 [num_pages, 64];
+    page_table: int32 [B, max_pages_per_seq] (-1 = none)."""
+    k_pages: torch.Tensor
+    v_pages: torch.Tensor
+    ts_pages: torch.Tensor
+    page_table: torch.Tensor
+
+    @staticmethod
+    def empty(num_pages, num_heads, head_dim, page_table, dtype=torch.bfloat16, device="cuda"):
+        k = torch.zeros(num_pages, num_heads, PAGE_SIZE, head_dim, dtype=dtype, device=device)
+        v = torch.zeros_like(k)
+        ts = torch.zeros(num_pages, PAGE_SIZE, dtype=torch.int64, device=device)
+        return PagedKVCache(k, v, ts, page_table)
+
+    def c_struct(self, params: LayerParams) -> _KVCache:
+        H, d = params.num_heads, params.head_dim
+        for name in ("k_pages", "v_pages"):
+            t = getattr(self, name)
+            _device_tensor(t, params.dtype, name)
+            if t.dim() != 4 or t.shape[1:] != (H, PAGE_SIZE, d):
+                raise ValueError(f"{name} must be [P, {H}, {PAGE_SIZE}, {d}]")
+        _device_tensor(self.ts_pages, torch.int64, "ts_pages")
+        _device_tensor(self.page_table, torch.int32, "page_table")
+        if self.page_table.dim() != 2:
+            raise ValueError("page_table must be [B, max_pages_per_seq]")
+        c = _KVCache()
+        c.k_pages, c.v_pages = self.k_pages.data_ptr(), self.v_pages.data_ptr()
+        c.ts_pages, c.page_table = self.ts_pages.data_ptr(), self.page_table.data_ptr()
+        c.num_pages = self.k_pages.shape[0]
+        c.page_size = PAGE_SIZE
+        c.max_pages_per_seq = self.page_table.shape[1]
+        return c
+
+
+def hstu_kv_append(cache: PagedKVCache, new_offsets, cache_lens, k_new, v_new, ts_new, params: LayerParams):
+    """Write new tokens' K, V, ts at positions cache_lens[b] + m of each user's pages."""
+    H, d = params.num_heads, params.head_dim
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _device_tensor(t, params.dtype, name)
+        if t.dim() != 3 or t.shape[1:] != (H, d):
+            raise ValueError(f"{name} must be [T, {H}, {d}]")
+    _device_tensor(ts_new, torch.int64, "ts_new")
+    _device_tensor(new_offsets, torch.int32, "new_offsets")
+    _device_tensor(cache_lens, torch.int32, "cache_lens")
+    c = cache.c_struct(params)
+    p = params.c_struct()
+    B = new_offsets.shape[0] - 1
+    _check(_lib.hstu_kv_append(ctypes.byref(c), ctypes.byref(p), B, new_offsets.data_ptr(), cache_lens.data_ptr(),
+                               k_new.shape[0], k_new.data_ptr(), v_new.data_ptr(), ts_new.data_ptr(), _stream()),
+           "hstu_kv_append")
+
+
+def hstu_attn_fwd_cached(q_new, u_new, ts_new, new_offsets, cache_lens, max_new: int, max_total: int,
+                         cache: PagedKVCache, params: LayerParams, *, y=None, workspace=None,
+                         timing_events=None):
+    """New tokens (already appended) attend causally to the cached prefix and themselves."""
+    H, d = params.num_heads, params.head_dim
+    _device_tensor(q_new, params.dtype, "q_new")
+    if q_new.dim() != 3 or q_new.shape[1:] != (H, d):
+        raise ValueError(f"q_new must be [T, {H}, {d}]")
+    _device_tensor(u_new, params.dtype, "u_new")
+    _device_tensor(ts_new, torch.int64, "ts_new")
+    _device_tensor(new_offsets, torch.int32, "new_offsets")
+    _device_tensor(cache_lens, torch.int32, "cache_lens")
+    T, B = q_new.shape[0], new_offsets.shape[0] - 1
+    y = torch.empty_like(u_new) if y is None else y
+    _device_tensor(y, params.dtype, "y")
+    nbytes = hstu_workspace_size(HSTU_FN_CACHED, params, B, T, max_total)
+    ws = _workspace(workspace, nbytes, q_new.device)
+    c = cache.c_struct(params)
+    p = params.c_struct(timing_events)
+    _check(_lib.hstu_attn_fwd_cached(ctypes.byref(p), B, new_offsets.data_ptr(), cache_lens.data_ptr(), max_new,
+                                     max_total, T, q_new.data_ptr(), u_new.data_ptr(), ts_new.data_ptr(),
+                                     ctypes.byref(c), y.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
+           "hstu_attn_fwd_cached")
+    return y
+
+
+def pair_count(kind: str, lengths: Sequence[int], extra: Optional[Sequence[int]] = None) -> int:
+    """Allowed (query, key) pairs per head: the unit of algorithmic work (4*d FLOP each).
+
+    full: sum L(L+1)/2; cached (lengths = new tokens, extra = cached prefix):
+    sum M*C + M(M+1)/2; mfalcon (lengths = history, extra = candidates):
+    sum n(n+1)/2 + m(n+1)."""
+    tot = 0
+    if kind == "full":
+        for L in lengths:
+            tot += L * (L + 1) // 2
+    elif kind == "cached":
+        for M, C in zip(lengths, extra):
+            tot += M * C + M * (M + 1) // 2
+    elif kind == "mfalcon":
+        for n, m in zip(lengths, extra):
+            tot += n * (n + 1) // 2 + m * (n + 1)
+    else:
+        raise ValueError(kind)
+    return int(tot)

@@ -1,0 +1,316 @@
+// C ABI of the HSTU attention library: host-side argument checks, workspace
+// layout and the launch sequence of each entry point. No allocation, no host
+// synchronisation; everything is queued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "../../include/hstu.h"
+#include "kernels.h"
+
+using namespace hstu;
+
+namespace {
+
+constexpr int32_t VERSION = 10000;  // 1.0.0
+constexpr int MAX_SPLITS = 16;      // key splits of the cached path
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+hstu_status_t check_params(const hstu_params_t* p) {
+  if (!p) return HSTU_ERR_INVALID_ARG;
+  if (p->num_heads < 1) return HSTU_ERR_INVALID_ARG;
+  if (p->dtype != HSTU_F32 && p->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
+  if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128) return HSTU_ERR_UNSUPPORTED;
+  if ((int64_t)p->num_heads * p->head_dim > 2048) return HSTU_ERR_UNSUPPORTED;
+  if (p->norm_n < 0) return HSTU_ERR_INVALID_ARG;
+  if (!(p->ln_eps > 0.0f)) return HSTU_ERR_INVALID_ARG;
+  if (p->pos_tab) {
+    if (p->n_pos < 1) return HSTU_ERR_INVALID_ARG;
+    if (p->n_pos > MAX_NPOS) return HSTU_ERR_UNSUPPORTED;
+    if (p->pos_head_stride != 0 && p->pos_head_stride < p->n_pos) return HSTU_ERR_INVALID_ARG;
+  }
+  if (p->time_tab) {
+    if (p->n_time < 1) return HSTU_ERR_INVALID_ARG;
+    if (p->time_head_stride != 0 && p->time_head_stride < p->n_time) return HSTU_ERR_INVALID_ARG;
+  }
+  if ((p->ln_w && !aligned16(p->ln_w)) || (p->ln_b && !aligned16(p->ln_b))) return HSTU_ERR_INVALID_ARG;
+  return HSTU_OK;
+}
+
+int cost_shift_for(int64_t max_keys) {
+  int64_t cost = ceil_div(max_keys, KT) + 1;
+  int s = 0;
+  while ((cost >> s) >= 1024) ++s;
+  return s;
+}
+
+// Key split of the cached path: at most MAX_SPLITS chunks of whole key tiles.
+int32_t chunk_keys_for(int64_t max_total) {
+  int64_t per = ceil_div(ceil_div(max_total, MAX_SPLITS), KT) * KT;
+  if (per < 8 * KT) per = 8 * KT;  // at least 512 keys per split
+  return (int32_t)per;
+}
+
+// Workspace layout of one call; returns false when the arguments overflow.
+bool layout(int fn, const hstu_params_t* p, int32_t B, int64_t Tq, int64_t max_len, WsLayout& w) {
+  if (B < 0 || Tq < 0 || max_len < 0) return false;
+  const int64_t H = p->num_heads, HD = (int64_t)p->num_heads * p->head_dim;
+  const int64_t tiles = ceil_div(Tq, QT) + B;  // bound on sum_b ceil(L_b / QT)
+  w.n_chunks = 1;
+  w.chunk_keys = 0;
+  if (fn == HSTU_FN_FULL) {
+    w.max_items = H * tiles;
+  } else if (fn == HSTU_FN_MFALCON) {
+    w.max_items = H * (tiles + B);
+  } else if (fn == HSTU_FN_CACHED) {
+    w.chunk_keys = chunk_keys_for(max_len);
+    w.n_chunks = (int32_t)(max_len > 0 ? ceil_div(max_len, w.chunk_keys) : 1);
+    w.max_items = H * tiles * w.n_chunks;
+  } else {
+    return false;
+  }
+  if (w.max_items > INT_MAX / 2) return false;
+  w.items_off = ALIGN;
+  w.scratch_off = align_up(w.items_off + (size_t)w.max_items * sizeof(WorkItem));
+  w.o_off = align_up(w.scratch_off + (size_t)(B + 1) * sizeof(int32_t));
+  w.total = align_up(w.o_off + (size_t)w.n_chunks * (size_t)Tq * (size_t)HD * sizeof(float));
+  return true;
+}
+
+AttnArgs base_args(const hstu_params_t* p, const WsLayout& w, void* ws, int64_t Tq) {
+  AttnArgs a = {};
+  a.pos_tab = p->pos_tab;
+  a.n_pos = p->n_pos;
+  a.pos_stride = p->pos_head_stride;
+  a.time_tab = p->time_tab;
+  a.n_time = p->n_time;
+  a.time_stride = p->time_head_stride;
+  a.alpha = p->alpha;
+  a.norm_n = p->norm_n;
+  a.H = p->num_heads;
+  a.Tq = Tq;
+  a.items = (const WorkItem*)((char*)ws + w.items_off);
+  a.count = (const int32_t*)ws;
+  a.o = (float*)((char*)ws + w.o_off);
+  a.o_chunk_stride = Tq * (int64_t)p->num_heads * p->head_dim;
+  a.n_chunks = w.n_chunks;
+  return a;
+}
+
+SchedArgs sched_args(int mode, const hstu_params_t* p, const WsLayout& w, void* ws, int32_t B,
+                     const int32_t* offsets, int64_t max_keys) {
+  SchedArgs s = {};
+  s.mode = mode;
+  s.B = B;
+  s.H = p->num_heads;
+  s.offsets = offsets;
+  s.chunk_keys = w.chunk_keys > 0 ? w.chunk_keys : KT;
+  s.cost_shift = cost_shift_for(max_keys);
+  s.max_items = w.max_items;
+  s.prefix = (int32_t*)((char*)ws + w.scratch_off);
+  s.items = (WorkItem*)((char*)ws + w.items_off);
+  s.count = (int32_t*)ws;
+  return s;
+}
+
+LnArgs ln_args(const hstu_params_t* p, const WsLayout& w, void* ws, const void* u, void* y, int64_t T) {
+  LnArgs l = {};
+  l.o = (const float*)((char*)ws + w.o_off);
+  l.o_chunk_stride = T * (int64_t)p->num_heads * p->head_dim;
+  l.u = u;
+  l.y = y;
+  l.ln_w = p->ln_w;
+  l.ln_b = p->ln_b;
+  l.eps = p->ln_eps;
+  l.HD = p->num_heads * p->head_dim;
+  l.T = T;
+  l.n_chunks = w.n_chunks;
+  return l;
+}
+
+hstu_status_t run_attention(const hstu_params_t* p, const SchedArgs& s, const AttnArgs& a, int mode,
+                            const LnArgs& l, hipStream_t stream) {
+  if (launch_sched(s, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  hipEvent_t ev0 = (hipEvent_t)p->timing_events[0], ev1 = (hipEvent_t)p->timing_events[1];
+  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  if (launch_attn(a, p->dtype, p->head_dim, mode, s.max_items, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  if (launch_ln_gate(l, p->dtype, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  return HSTU_OK;
+}
+
+bool any_null(std::initializer_list<const void*> ps) {
+  for (const void* x : ps)
+    if (!x) return true;
+  return false;
+}
+
+bool any_misaligned(std::initializer_list<const void*> ps) {
+  for (const void* x : ps)
+    if (!aligned16(x)) return true;
+  return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hstu_status_string(hstu_status_t s) {
+  switch (s) {
+    case HSTU_OK: return "HSTU_OK";
+    case HSTU_ERR_INVALID_ARG: return "HSTU_ERR_INVALID_ARG: invalid argument";
+    case HSTU_ERR_UNSUPPORTED: return "HSTU_ERR_UNSUPPORTED: unsupported dtype, head_dim or table size";
+    case HSTU_ERR_WORKSPACE: return "HSTU_ERR_WORKSPACE: workspace missing or too small";
+    case HSTU_ERR_LAUNCH: return "HSTU_ERR_LAUNCH: kernel launch failed";
+  }
+  return "HSTU: unknown status";
+}
+
+int32_t hstu_version(void) { return VERSION; }
+
+size_t hstu_workspace_size(int32_t fn, const hstu_params_t* params, int32_t batch, int64_t total_q_tokens,
+                           int32_t max_len) {
+  if (check_params(params) != HSTU_OK) return 0;
+  WsLayout w;
+  if (!layout(fn, params, batch, total_q_tokens, max_len, w)) return 0;
+  return w.total;
+}
+
+hstu_status_t hstu_attn_fwd(const hstu_params_t* params, int32_t batch, const int32_t* seq_offsets,
+                            int32_t max_len, int64_t total_tokens, const void* q, const void* k,
+                            const void* v, const void* u, const int64_t* ts, void* y, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  hstu_status_t st = check_params(params);
+  if (st != HSTU_OK) return st;
+  if (batch < 0 || total_tokens < 0 || max_len < 0) return HSTU_ERR_INVALID_ARG;
+  if (batch == 0 || total_tokens == 0) return HSTU_OK;
+  if (any_null({seq_offsets, q, k, v, u, ts, y})) return HSTU_ERR_INVALID_ARG;
+  if (any_misaligned({q, k, v, u, ts, y})) return HSTU_ERR_INVALID_ARG;
+  WsLayout w;
+  if (!layout(HSTU_FN_FULL, params, batch, total_tokens, max_len, w)) return HSTU_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < w.total || !aligned16(ws)) return HSTU_ERR_WORKSPACE;
+
+  SchedArgs s = sched_args(MODE_FULL, params, w, ws, batch, seq_offsets, max_len);
+  AttnArgs a = base_args(params, w, ws, total_tokens);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.ts = ts;
+  a.offsets = seq_offsets;
+  LnArgs l = ln_args(params, w, ws, u, y, total_tokens);
+  return run_attention(params, s, a, MODE_FULL, l, stream);
+}
+
+hstu_status_t hstu_mfalcon_fwd(const hstu_params_t* params, int32_t batch, const int32_t* seq_offsets,
+                               const int32_t* num_candidates, int32_t max_len, int64_t total_tokens,
+                               const void* q, const void* k, const void* v, const void* u,
+                               const int64_t* ts, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hstu_status_t st = check_params(params);
+  if (st != HSTU_OK) return st;
+  if (batch < 0 || total_tokens < 0 || max_len < 0) return HSTU_ERR_INVALID_ARG;
+  if (batch == 0 || total_tokens == 0) return HSTU_OK;
+  if (any_null({seq_offsets, num_candidates, q, k, v, u, ts, y})) return HSTU_ERR_INVALID_ARG;
+  if (any_misaligned({q, k, v, u, ts, y})) return HSTU_ERR_INVALID_ARG;
+  WsLayout w;
+  if (!layout(HSTU_FN_MFALCON, params, batch, total_tokens, max_len, w)) return HSTU_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < w.total || !aligned16(ws)) return HSTU_ERR_WORKSPACE;
+
+  SchedArgs s = sched_args(MODE_MFALCON, params, w, ws, batch, seq_offsets, max_len);
+  s.num_cand = num_candidates;
+  AttnArgs a = base_args(params, w, ws, total_tokens);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.ts = ts;
+  a.offsets = seq_offsets;
+  a.num_cand = num_candidates;
+  LnArgs l = ln_args(params, w, ws, u, y, total_tokens);
+  return run_attention(params, s, a, MODE_MFALCON, l, stream);
+}
+
+hstu_status_t hstu_kv_append(const hstu_kv_cache_t* cache, const hstu_params_t* params, int32_t batch,
+                             const int32_t* new_offsets, const int32_t* cache_lens, int64_t total_new,
+                             const void* k_new, const void* v_new, const int64_t* ts_new,
+                             hipStream_t stream) {
+  hstu_status_t st = check_params(params);
+  if (st != HSTU_OK) return st;
+  if (!cache) return HSTU_ERR_INVALID_ARG;
+  if (cache->page_size != PAGE) return HSTU_ERR_UNSUPPORTED;
+  if (batch < 0 || total_new < 0 || cache->num_pages < 0 || cache->max_pages_per_seq < 0)
+    return HSTU_ERR_INVALID_ARG;
+  if (batch == 0 || total_new == 0) return HSTU_OK;
+  if (any_null({cache->k_pages, cache->v_pages, cache->ts_pages, cache->page_table, new_offsets, cache_lens,
+                k_new, v_new, ts_new}))
+    return HSTU_ERR_INVALID_ARG;
+  if (any_misaligned({cache->k_pages, cache->v_pages, cache->ts_pages, k_new, v_new, ts_new}))
+    return HSTU_ERR_INVALID_ARG;
+  AppendArgs a = {};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.ts_new = ts_new;
+  a.offsets = new_offsets;
+  a.cache_lens = cache_lens;
+  a.k_pages = cache->k_pages;
+  a.v_pages = cache->v_pages;
+  a.ts_pages = cache->ts_pages;
+  a.page_table = cache->page_table;
+  a.num_pages = cache->num_pages;
+  a.max_pages = cache->max_pages_per_seq;
+  a.B = batch;
+  a.H = params->num_heads;
+  a.D = params->head_dim;
+  a.elem_bytes = params->dtype == HSTU_BF16 ? 2 : 4;
+  a.T = total_new;
+  return launch_kv_append(a, stream) == hipSuccess ? HSTU_OK : HSTU_ERR_LAUNCH;
+}
+
+hstu_status_t hstu_attn_fwd_cached(const hstu_params_t* params, int32_t batch, const int32_t* new_offsets,
+                                   const int32_t* cache_lens, int32_t max_new, int32_t max_total,
+                                   int64_t total_new, const void* q_new, const void* u_new,
+                                   const int64_t* ts_new, const hstu_kv_cache_t* cache, void* y_new,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  hstu_status_t st = check_params(params);
+  if (st != HSTU_OK) return st;
+  if (!cache) return HSTU_ERR_INVALID_ARG;
+  if (cache->page_size != PAGE) return HSTU_ERR_UNSUPPORTED;
+  if (batch < 0 || total_new < 0 || max_new < 0 || max_total < 0 || cache->num_pages < 0 ||
+      cache->max_pages_per_seq < 0)
+    return HSTU_ERR_INVALID_ARG;
+  if (batch == 0 || total_new == 0) return HSTU_OK;
+  if (any_null({cache->k_pages, cache->v_pages, cache->ts_pages, cache->page_table, new_offsets, cache_lens,
+                q_new, u_new, ts_new, y_new}))
+    return HSTU_ERR_INVALID_ARG;
+  if (any_misaligned({cache->k_pages, cache->v_pages, cache->ts_pages, q_new, u_new, ts_new, y_new}))
+    return HSTU_ERR_INVALID_ARG;
+  if ((int64_t)cache->max_pages_per_seq * PAGE < max_total) return HSTU_ERR_INVALID_ARG;
+  WsLayout w;
+  if (!layout(HSTU_FN_CACHED, params, batch, total_new, max_total, w)) return HSTU_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < w.total || !aligned16(ws)) return HSTU_ERR_WORKSPACE;
+
+  SchedArgs s = sched_args(MODE_CACHED, params, w, ws, batch, new_offsets, w.chunk_keys);
+  s.cache_lens = cache_lens;
+  AttnArgs a = base_args(params, w, ws, total_new);
+  a.q = q_new;
+  a.ts = ts_new;
+  a.offsets = new_offsets;
+  a.cache_lens = cache_lens;
+  a.k_pages = cache->k_pages;
+  a.v_pages = cache->v_pages;
+  a.ts_pages = cache->ts_pages;
+  a.page_table = cache->page_table;
+  a.num_pages = cache->num_pages;
+  a.max_pages = cache->max_pages_per_seq;
+  LnArgs l = ln_args(params, w, ws, u_new, y_new, total_new);
+  l.chunk_keys = w.chunk_keys;
+  l.B = batch;
+  l.offsets = new_offsets;
+  l.cache_lens = cache_lens;
+  return run_attention(params, s, a, MODE_CACHED, l, stream);
+}
+
+}  // extern "C"

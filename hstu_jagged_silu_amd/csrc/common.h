@@ -1,0 +1,55 @@
+// Shared device-side definitions of the HSTU attention library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hstu {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+// Which attention variant a launch computes.
+enum Mode : int32_t { MODE_FULL = 0, MODE_CACHED = 1, MODE_MFALCON = 2 };
+
+// Kinds of query tile: causal rows (full path, cached new tokens, M-FALCON
+// history) or M-FALCON candidate rows.
+enum Kind : int32_t { KIND_CAUSAL = 0, KIND_CANDIDATE = 1 };
+
+// Tile geometry: a workgroup of 4 wave64s owns QT query rows (32 per wave)
+// and walks the keys in tiles of KT.
+constexpr int QT = 128;
+constexpr int KT = 64;
+constexpr int NWAVES = 4;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int MAX_NPOS = 2048;
+constexpr int PAGE = 64;           // page size of the paged KV cache (one key tile)
+
+// One unit of attention work: query rows [q_start, q_start + q_len) of user
+// b (local indices), head h, against keys [k_begin, k_end). `chunk` numbers
+// the key split of the KV-cache path (0 elsewhere).
+struct WorkItem {
+  int32_t b, h, chunk, kind;
+  int32_t q_start, q_len, k_begin, k_end;
+};
+
+// Workspace layout (bytes), shared by the scheduler, the attention kernel
+// and the epilogue: [header 256 B][items][per-user scratch][O partials].
+struct WsLayout {
+  size_t items_off, scratch_off, o_off, total;
+  int64_t max_items;
+  int32_t n_chunks;       // key splits (1 except on the cached path)
+  int32_t chunk_keys;     // keys per split (multiple of KT)
+};
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// log2(e) and ln(2) in float
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+}  // namespace hstu

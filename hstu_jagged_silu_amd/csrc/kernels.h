@@ -1,0 +1,91 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include "common.h"
+
+namespace hstu {
+
+// Arguments of the fused attention kernel (passed by value).
+struct AttnArgs {
+  const void* q;                 // [Tq, H, D] query rows
+  const void* k;                 // [Tk, H, D] keys (jagged variants)
+  const void* v;
+  const int64_t* ts;             // [Tq] query timestamps (also key timestamps when jagged)
+  const int32_t* offsets;        // [B+1] query row offsets
+  const int32_t* cache_lens;     // [B] cached path
+  const int32_t* num_cand;       // [B] M-FALCON
+  const void* k_pages;           // [P, H, 64, D] cached path
+  const void* v_pages;
+  const int64_t* ts_pages;       // [P, 64]
+  const int32_t* page_table;     // [B, max_pages]
+  int32_t num_pages, max_pages;
+  const float* pos_tab;
+  int32_t n_pos, pos_stride;
+  const float* time_tab;
+  int32_t n_time, time_stride;
+  float alpha;
+  int32_t norm_n;
+  int32_t H;
+  int64_t Tq;                    // number of query rows
+  const WorkItem* items;
+  const int32_t* count;          // number of valid items
+  float* o;                      // [n_chunks][Tq][H*D] fp32, scaled attention output
+  int64_t o_chunk_stride;        // elements between key splits
+  int32_t n_chunks;              // key splits the O buffer holds
+};
+
+// Arguments of the single-workgroup jagged tile scheduler.
+struct SchedArgs {
+  int32_t mode;
+  int32_t B, H;
+  const int32_t* offsets;        // [B+1] query rows
+  const int32_t* cache_lens;     // cached path
+  const int32_t* num_cand;       // M-FALCON
+  int32_t chunk_keys;            // key split (cached path), multiple of KT
+  int32_t cost_shift;            // cost bin = min(cost >> shift, NBINS - 1)
+  int64_t max_items;
+  int32_t* prefix;               // [B+1] scratch
+  WorkItem* items;
+  int32_t* count;
+};
+
+// Arguments of the LayerNorm + U gating epilogue (sums key splits first).
+struct LnArgs {
+  const float* o;                // [n_chunks][T][HD]
+  int64_t o_chunk_stride;
+  const void* u;                 // [T, HD]
+  void* y;                       // [T, HD]
+  const float* ln_w;
+  const float* ln_b;
+  float eps;
+  int32_t HD;
+  int64_t T;
+  // split bookkeeping (cached path); chunk_keys == 0 means one split
+  int32_t chunk_keys;
+  int32_t n_chunks;
+  int32_t B;
+  const int32_t* offsets;
+  const int32_t* cache_lens;
+};
+
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  const int64_t* ts_new;
+  const int32_t* offsets;        // [B+1] new rows
+  const int32_t* cache_lens;     // [B]
+  void* k_pages;
+  void* v_pages;
+  int64_t* ts_pages;
+  const int32_t* page_table;
+  int32_t num_pages, max_pages;
+  int32_t B, H, D, elem_bytes;
+  int64_t T;
+};
+
+hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int mode, int64_t grid, hipStream_t s);
+hipError_t launch_ln_gate(const LnArgs& a, int dtype, hipStream_t s);
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
+
+}  // namespace hstu

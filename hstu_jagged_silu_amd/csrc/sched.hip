@@ -1,0 +1,187 @@
+// Jagged tile scheduler: turns per-user lengths (device memory) into the
+// attention work list, ordered longest first.
+//
+// User histories differ wildly in length ("HSTU Generative Recommenders:
+// Deploy on GPU Cloud", section "Scaling Training and Serving Across
+// Multiple GPUs", on sequence-length balancing). A causal query tile at row r
+// costs about r / 64 key tiles, so the attention grid is launched over the
+// items sorted by decreasing cost: the hardware dispatcher then hands the
+// next-longest item to whichever compute unit frees up first (greedy longest
+// processing time). Masked key tiles are never listed (causal tile skipping):
+// an item's key range ends at its last row's limit.
+//
+// One workgroup of 1024 threads: count items per user, scan, histogram the
+// costs, scan the histogram from the top, scatter. Runs on the caller's
+// stream ahead of the attention kernel; no host synchronisation.
+#include "kernels.h"
+
+namespace hstu {
+
+constexpr int SCHED_THREADS = 1024;
+constexpr int NBINS = 1024;
+
+struct UserGeo {
+  int nq_causal;   // causal query tiles
+  int nq_cand;     // candidate query tiles (M-FALCON)
+  int L, C, n;     // rows, cached prefix, history length
+};
+
+__device__ inline UserGeo user_geo(const SchedArgs& a, int b) {
+  UserGeo g;
+  g.L = max(0, a.offsets[b + 1] - a.offsets[b]);
+  g.C = (a.mode == MODE_CACHED) ? a.cache_lens[b] : 0;
+  g.n = g.L;
+  g.nq_cand = 0;
+  if (a.mode == MODE_MFALCON) {
+    const int m = min(max(a.num_cand[b], 0), g.L);
+    g.n = g.L - m;
+    g.nq_cand = (int)ceil_div(m, QT);
+  }
+  g.nq_causal = (int)ceil_div(g.n, QT);
+  return g;
+}
+
+// key splits of causal tile qt on the cached path
+__device__ inline int tile_chunks(const SchedArgs& a, const UserGeo& g, int qt) {
+  if (a.mode != MODE_CACHED) return 1;
+  const int kend = g.C + min((qt + 1) * QT, g.n);
+  return (int)ceil_div(kend, a.chunk_keys);
+}
+
+__device__ inline int user_items_per_head(const SchedArgs& a, const UserGeo& g) {
+  if (a.mode != MODE_CACHED) return g.nq_causal + g.nq_cand;
+  int s = 0;
+  for (int qt = 0; qt < g.nq_causal; ++qt) s += tile_chunks(a, g, qt);
+  return s;
+}
+
+// the local-th item of user b
+__device__ inline WorkItem make_item(const SchedArgs& a, int b, int local) {
+  const UserGeo g = user_geo(a, b);
+  const int per_head = user_items_per_head(a, g);
+  WorkItem w;
+  w.b = b;
+  w.h = local / per_head;
+  int t = local % per_head;
+  w.chunk = 0;
+  w.kind = KIND_CAUSAL;
+  if (a.mode == MODE_CACHED) {
+    int qt = 0;
+    while (t >= tile_chunks(a, g, qt)) { t -= tile_chunks(a, g, qt); ++qt; }
+    w.q_start = qt * QT;
+    w.q_len = min(QT, g.n - w.q_start);
+    const int kend = g.C + w.q_start + w.q_len;
+    w.chunk = t;
+    w.k_begin = t * a.chunk_keys;
+    w.k_end = min(kend, (t + 1) * a.chunk_keys);
+  } else if (t < g.nq_causal) {
+    w.q_start = t * QT;
+    w.q_len = min(QT, g.n - w.q_start);
+    w.k_begin = 0;
+    w.k_end = w.q_start + w.q_len;
+  } else {
+    const int qc = t - g.nq_causal;
+    w.kind = KIND_CANDIDATE;
+    w.q_start = g.n + qc * QT;
+    w.q_len = min(QT, g.L - w.q_start);
+    w.k_begin = 0;
+    w.k_end = g.n;
+  }
+  return w;
+}
+
+__device__ inline int item_bin(const SchedArgs& a, const WorkItem& w) {
+  const int cost = (int)ceil_div(max(w.k_end - w.k_begin, 0), KT) + 1;
+  return min(cost >> a.cost_shift, NBINS - 1);
+}
+
+// block-wide exclusive scan of one value per thread; returns the block total
+__device__ inline int block_scan(int x, int* tmp, int& excl) {
+  const int tid = threadIdx.x;
+  tmp[tid] = x;
+  __syncthreads();
+  for (int off = 1; off < SCHED_THREADS; off <<= 1) {
+    const int y = tid >= off ? tmp[tid - off] : 0;
+    __syncthreads();
+    tmp[tid] += y;
+    __syncthreads();
+  }
+  excl = tmp[tid] - x;
+  const int total = tmp[SCHED_THREADS - 1];
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(SchedArgs a) {
+  __shared__ int tmp[SCHED_THREADS];
+  __shared__ int hist[NBINS];
+  __shared__ int start[NBINS];
+  const int tid = threadIdx.x;
+
+  // 1. items per user -> exclusive prefix over users
+  int carry = 0;
+  for (int base = 0; base < a.B; base += SCHED_THREADS) {
+    const int b = base + tid;
+    int c = 0;
+    if (b < a.B) c = a.H * user_items_per_head(a, user_geo(a, b));
+    int excl;
+    const int tot = block_scan(c, tmp, excl);
+    if (b < a.B) a.prefix[b] = carry + excl;
+    carry += tot;
+  }
+  int total = carry;
+  if ((int64_t)total > a.max_items) total = (int)a.max_items;  // cannot happen with a valid bound
+  if (tid == 0) a.prefix[a.B] = carry;
+  for (int i = tid; i < NBINS; i += SCHED_THREADS) hist[i] = 0;
+  __threadfence_block();
+  __syncthreads();
+
+  auto user_of = [&](int g) {
+    int lo = 0, hi = a.B - 1;  // largest b with prefix[b] <= g
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.prefix[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+
+  // 2. cost histogram
+  for (int g = tid; g < total; g += SCHED_THREADS) {
+    const int b = user_of(g);
+    const WorkItem w = make_item(a, b, g - a.prefix[b]);
+    atomicAdd(&hist[item_bin(a, w)], 1);
+  }
+  __syncthreads();
+
+  // 3. start of each bin, most expensive bin first
+  {
+    const int per = NBINS / SCHED_THREADS;  // bins per thread (1)
+    int s = 0;
+    for (int i = 0; i < per; ++i) s += hist[NBINS - 1 - (tid * per + i)];
+    int excl;
+    block_scan(s, tmp, excl);
+    int acc = excl;
+    for (int i = 0; i < per; ++i) {
+      const int bin = NBINS - 1 - (tid * per + i);
+      start[bin] = acc;
+      acc += hist[bin];
+    }
+  }
+  __syncthreads();
+
+  // 4. scatter
+  for (int g = tid; g < total; g += SCHED_THREADS) {
+    const int b = user_of(g);
+    const WorkItem w = make_item(a, b, g - a.prefix[b]);
+    const int pos = atomicAdd(&start[item_bin(a, w)], 1);
+    a.items[pos] = w;
+  }
+  if (tid == 0) *a.count = total;
+}
+
+hipError_t launch_sched(const SchedArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(SCHED_THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hstu

@@ -1,0 +1,223 @@
+/*
+ * hstu.h - C ABI of the HSTU attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes HSTU pointwise SiLU attention over jagged user
+ * sequences and its two serving variants. The operation, per user sequence b
+ * and head h (local indices, keys j allowed by the mask of the variant):
+ *
+ *   s_ij = alpha * <q_i, k_j> + P[min(p_i - p_j, n_pos - 1)]
+ *                             + T[min(floor(log2(|ts_i - ts_j| + 1)), n_time - 1)]
+ *   o_i  = sum_j SiLU(s_ij) / N_b * v_j          (masked pairs contribute 0)
+ *   y_i  = (LayerNorm_{H*d}(o_i) * ln_w + ln_b) (elementwise *) u_i
+ *
+ * Sources. SiLU weighting in place of softmax, relative attention bias and
+ * elementwise gating before the output projection: "Generative recommenders
+ * at scale", section "Inside NVIDIA's GPU-native stack for HSTU and Semantic
+ * IDs", and "How Generative Recommenders Are Redefining RecSys at Scale",
+ * Takeaways. Timestamp-ordered user histories: the latter page's
+ * description. Reuse of a cached prefix with a paged GPU table and append:
+ * "Deploying an HSTU Generative Recommender with NVIDIA Dynamo-Triton",
+ * section "Technical Stack and Performance Gains", and page
+ * "recomendador-generativo-hstu-dynamo-triton", section "Como o recomendador
+ * generativo HSTU reutiliza o histórico". M-FALCON candidate scoring by a
+ * changed mask and bias: "HSTU Generative Recommenders: Deploy on GPU Cloud",
+ * section "M-FALCON: Microbatched Attention for Scoring Multiple Candidates
+ * at Once". The pages print no formula; N_b, the bucket functions and the
+ * norm are the plain readings stated with each entry point.
+ *
+ * Conventions shared by every entry point
+ *   - Tokens are packed back to back ("jagged"): Q, K, V are [T, H, d] row
+ *     major (d fastest), U and Y are [T, H*d]. seq_offsets[b] is the first row
+ *     of user b, seq_offsets[0] = 0, seq_offsets[B] = T, non-decreasing.
+ *   - dtype HSTU_BF16: Q, K, V, U, Y and the K/V pages hold bf16; arithmetic
+ *     is bf16 products with fp32 accumulation (the SiLU weights are rounded
+ *     to bf16 before the second product). HSTU_F32: everything fp32.
+ *   - All pointers except `params` and the hstu_kv_cache_t struct itself are
+ *     device pointers. Bias tables, LayerNorm weights, offsets, lengths and
+ *     the page table are device memory too.
+ *   - Every call is asynchronous on `stream`, performs no host
+ *     synchronisation and allocates nothing: the caller owns all buffers,
+ *     including the workspace. Calls with different workspaces may run
+ *     concurrently; calls sharing a workspace must be ordered on one stream.
+ *   - Errors: argument checks run on the host before anything is launched and
+ *     return a status; nothing is launched then. HSTU_ERR_LAUNCH reports a
+ *     failed kernel launch. Device-side content (offsets, lengths, page
+ *     indices, timestamps) is trusted: page indices outside [0, num_pages)
+ *     read as zero keys and are never written, rows beyond T are never read,
+ *     but inconsistent offsets give unspecified values in Y.
+ *   - Timestamps are int64 seconds. Within one user any two timestamps must
+ *     differ by less than 2^62.
+ */
+#ifndef HSTU_H_
+#define HSTU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_ERR_INVALID_ARG = 1,  /* NULL pointer, negative size, bad alignment  */
+  HSTU_ERR_UNSUPPORTED = 2,  /* dtype / head_dim / table size not supported */
+  HSTU_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required  */
+  HSTU_ERR_LAUNCH = 4        /* a kernel launch failed                      */
+} hstu_status_t;
+
+typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype_t;
+
+/* Which entry point a workspace is sized for. */
+typedef enum { HSTU_FN_FULL = 0, HSTU_FN_CACHED = 1, HSTU_FN_MFALCON = 2 } hstu_fn_t;
+
+/*
+ * Layer parameters shared by every attention entry point.
+ *   num_heads     H >= 1
+ *   head_dim      d in {32, 64, 128}; H*d <= 2048
+ *   dtype         hstu_dtype_t
+ *   alpha         scale of <q, k>; 1.0 in the plain reading
+ *   norm_n        0: N_b is per user (full: L_b; cached: C_b + M_b;
+ *                 M-FALCON: n_b + 1). > 0: that fixed N for every user.
+ *   pos_tab       NULL (no position bias) or fp32 [H][pos_head_stride] with
+ *                 n_pos valid entries per head; pos_head_stride = 0 shares one
+ *                 table across heads. 1 <= n_pos <= 2048.
+ *   time_tab      NULL (no time bias) or fp32 likewise; n_time >= 1 (entries
+ *                 beyond index 63 are unreachable for int64 seconds).
+ *   ln_w, ln_b    NULL for 1 / 0, else fp32 [H*d] affine terms of the norm.
+ *   ln_eps        LayerNorm epsilon (1e-5 in the plain reading), > 0.
+ *   timing_events optional pair of hipEvent_t (cast to void*) recorded on the
+ *                 stream immediately before and after the fused attention
+ *                 kernel, for timing that kernel alone; NULL to skip.
+ */
+typedef struct {
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t dtype;
+  float alpha;
+  int32_t norm_n;
+  const float* pos_tab;
+  int32_t n_pos;
+  int32_t pos_head_stride;
+  const float* time_tab;
+  int32_t n_time;
+  int32_t time_head_stride;
+  const float* ln_w;
+  const float* ln_b;
+  float ln_eps;
+  void* timing_events[2];
+} hstu_params_t;
+
+/*
+ * Paged KV cache ("paged GPU table", page "recomendador-generativo-hstu-
+ * dynamo-triton", section "Como o recomendador generativo HSTU reutiliza o
+ * histórico"). Logical token position p of user b lives in page
+ * page_table[b * max_pages_per_seq + p / page_size] at slot p % page_size.
+ *   k_pages, v_pages  [num_pages, H, page_size, d] in the layer dtype
+ *   ts_pages          int64 [num_pages, page_size]
+ *   page_table        int32 [batch, max_pages_per_seq]; -1 = no page
+ *   page_size         must be 64
+ * The caller owns the pages and the table and decides which pages a user
+ * holds; the library never allocates, frees or evicts pages.
+ */
+typedef struct {
+  void* k_pages;
+  void* v_pages;
+  int64_t* ts_pages;
+  const int32_t* page_table;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t max_pages_per_seq;
+} hstu_kv_cache_t;
+
+/* Human-readable name of a status code (static string). */
+const char* hstu_status_string(hstu_status_t status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t hstu_version(void);
+
+/*
+ * Workspace bytes needed by one call of entry point `fn`.
+ *   batch           number of users B
+ *   total_q_tokens  query rows T (full, M-FALCON) or new rows (cached)
+ *   max_len         longest user: L (full), history + candidates (M-FALCON),
+ *                   cache_len + new tokens (cached)
+ * Returns 0 when the arguments are invalid. The value depends only on the
+ * arguments, so a workspace sized once for the largest call serves all
+ * smaller ones.
+ */
+size_t hstu_workspace_size(int32_t fn, const hstu_params_t* params, int32_t batch,
+                           int64_t total_q_tokens, int32_t max_len);
+
+/*
+ * Full causal path: every token attends to itself and the earlier tokens of
+ * its own user; N_b = L_b (unless params->norm_n > 0).
+ *   seq_offsets  int32 [batch + 1]
+ *   max_len      >= every L_b (only used to size the launch)
+ *   total_tokens T = seq_offsets[batch]
+ *   q, k, v      [T, H, d]; u, y: [T, H*d]; ts: int64 [T]
+ *   ws, ws_bytes workspace of at least hstu_workspace_size(HSTU_FN_FULL, ...)
+ * y must not alias any input. All tensors 16-byte aligned.
+ */
+hstu_status_t hstu_attn_fwd(const hstu_params_t* params, int32_t batch, const int32_t* seq_offsets,
+                            int32_t max_len, int64_t total_tokens, const void* q, const void* k,
+                            const void* v, const void* u, const int64_t* ts, void* y, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Paged KV append: new token m of user b (packed row new_offsets[b] + m)
+ * is written at logical position cache_lens[b] + m of that user's pages:
+ * its K and V rows for every head, and its timestamp.
+ *   new_offsets  int32 [batch + 1] over the packed new tokens
+ *   cache_lens   int32 [batch], length of each user's cache before this call
+ *   k_new, v_new [T_new, H, d]; ts_new int64 [T_new]
+ * The table must already hold pages for positions up to cache_lens[b] +
+ * M_b - 1; positions whose page index is outside [0, num_pages) are skipped.
+ * cache_lens is not updated (the caller advances it).
+ */
+hstu_status_t hstu_kv_append(const hstu_kv_cache_t* cache, const hstu_params_t* params, int32_t batch,
+                             const int32_t* new_offsets, const int32_t* cache_lens, int64_t total_new,
+                             const void* k_new, const void* v_new, const int64_t* ts_new,
+                             hipStream_t stream);
+
+/*
+ * KV-cache delta path: the M_b new tokens of user b, already appended with
+ * hstu_kv_append, attend causally to the C_b = cache_lens[b] cached tokens
+ * and to themselves. Query m sits at position C_b + m and sees keys
+ * 0 .. C_b + m, all read from the pages; N_b = C_b + M_b. The result equals
+ * rows C_b .. C_b + M_b - 1 of the full path over the user's C_b + M_b
+ * tokens.
+ *   new_offsets  int32 [batch + 1] over the packed new tokens
+ *   max_new      >= every M_b;  max_total >= every C_b + M_b
+ *   q_new        [T_new, H, d]; u_new, y_new [T_new, H*d]; ts_new int64 [T_new]
+ */
+hstu_status_t hstu_attn_fwd_cached(const hstu_params_t* params, int32_t batch, const int32_t* new_offsets,
+                                   const int32_t* cache_lens, int32_t max_new, int32_t max_total,
+                                   int64_t total_new, const void* q_new, const void* u_new,
+                                   const int64_t* ts_new, const hstu_kv_cache_t* cache, void* y_new,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * M-FALCON candidate path. User b spans rows [history (n_b) | candidates
+ * (m_b = num_candidates[b])]. History rows are causal over the history.
+ * Every candidate sits at position n_b, attends to all n_b history keys
+ * (relative position n_b - j) and to itself (relative position 0, time
+ * difference 0), and to no other candidate. N_b = n_b + 1 for all rows of
+ * the user. Each candidate row therefore equals the last row of the full
+ * path on [history | that candidate].
+ *   num_candidates  int32 [batch], 0 <= m_b <= L_b
+ *   other arguments as in hstu_attn_fwd (max_len >= n_b + m_b)
+ */
+hstu_status_t hstu_mfalcon_fwd(const hstu_params_t* params, int32_t batch, const int32_t* seq_offsets,
+                               const int32_t* num_candidates, int32_t max_len, int64_t total_tokens,
+                               const void* q, const void* k, const void* v, const void* u,
+                               const int64_t* ts, void* y, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H_ */

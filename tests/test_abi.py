@@ -1,0 +1,177 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, the binding's structs match the C layout, and host-side
+argument validation returns the documented status before anything launches."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu.h")
+
+hs = pytest.importorskip("hstu_jagged_silu_amd")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hstu_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("hstu_attn_fwd", "hstu_attn_fwd_cached", "hstu_mfalcon_fwd", "hstu_kv_append",
+              "hstu_workspace_size", "hstu_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    lib = hs.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", hs.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (hstu_\w+)", out))
+    assert set(declared_functions()) <= exported
+    assert set(hs.EXPORTED_SYMBOLS) == set(declared_functions())
+
+
+def test_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "hstu.h"
+#define P(s, f) printf(#s "." #f " %zu\n", offsetof(s, f))
+int main(void) {
+  printf("hstu_params_t %zu\n", sizeof(hstu_params_t));
+  P(hstu_params_t, num_heads); P(hstu_params_t, head_dim); P(hstu_params_t, dtype); P(hstu_params_t, alpha);
+  P(hstu_params_t, norm_n); P(hstu_params_t, pos_tab); P(hstu_params_t, n_pos); P(hstu_params_t, pos_head_stride);
+  P(hstu_params_t, time_tab); P(hstu_params_t, n_time); P(hstu_params_t, time_head_stride);
+  P(hstu_params_t, ln_w); P(hstu_params_t, ln_b); P(hstu_params_t, ln_eps); P(hstu_params_t, timing_events);
+  printf("hstu_kv_cache_t %zu\n", sizeof(hstu_kv_cache_t));
+  P(hstu_kv_cache_t, k_pages); P(hstu_kv_cache_t, v_pages); P(hstu_kv_cache_t, ts_pages);
+  P(hstu_kv_cache_t, page_table); P(hstu_kv_cache_t, num_pages); P(hstu_kv_cache_t, page_size);
+  P(hstu_kv_cache_t, max_pages_per_seq);
+  return 0;
+}
+''')
+    exe = tmp_path / "layout"
+    r = subprocess.run(["gcc", "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", str(src), "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    lines = subprocess.run([str(exe)], capture_output=True, text=True).stdout.split("\n")
+    got = dict(l.rsplit(" ", 1) for l in lines if l)
+    assert int(got["hstu_params_t"]) == ctypes.sizeof(hs._Params)
+    assert int(got["hstu_kv_cache_t"]) == ctypes.sizeof(hs._KVCache)
+    for name, _ in hs._Params._fields_:
+        assert int(got[f"hstu_params_t.{name}"]) == getattr(hs._Params, name).offset, name
+    for name, _ in hs._KVCache._fields_:
+        assert int(got[f"hstu_kv_cache_t.{name}"]) == getattr(hs._KVCache, name).offset, name
+
+
+def test_version_and_status_strings():
+    assert hs.version() == 10000
+    for code in range(5):
+        assert hs.status_string(code).startswith("HSTU")
+    assert "unknown" in hs.status_string(99)
+
+
+def _params(**kw):
+    p = hs._Params()
+    p.num_heads, p.head_dim, p.dtype, p.alpha, p.norm_n, p.ln_eps = 4, 128, 1, 1.0, 0, 1e-5
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _ws(fn, p, B, T, L):
+    return int(hs.lib().hstu_workspace_size(fn, ctypes.byref(p), B, T, L))
+
+
+def test_workspace_size_valid_and_invalid():
+    p = _params()
+    full = _ws(0, p, 8, 65536, 8192)
+    # header + items + per-user scratch + fp32 O of T x H*d
+    assert full >= 65536 * 512 * 4
+    assert full % 256 == 0
+    assert _ws(0, p, 8, 65536, 8192) == full              # deterministic
+    assert _ws(0, p, 16, 65536, 8192) >= full              # more users, more items
+    assert _ws(0, p, 8, 131072, 8192) > full               # more tokens
+    cached = _ws(1, p, 8, 1024, 8320)
+    assert cached >= 1024 * 512 * 4 * 2                    # at least two key splits of O
+    assert _ws(2, p, 4, 20480, 5120) >= 20480 * 512 * 4
+    assert _ws(7, p, 8, 1024, 1024) == 0                   # unknown entry point
+    assert _ws(0, _params(dtype=5), 8, 1024, 128) == 0      # unknown dtype
+    assert _ws(0, _params(head_dim=48), 8, 1024, 128) == 0  # unsupported head dim
+    assert _ws(0, _params(num_heads=32), 8, 1024, 128) == 0  # H*d > 2048
+    assert _ws(0, _params(num_heads=0), 8, 1024, 128) == 0
+    assert _ws(0, p, -1, 1024, 128) == 0
+    assert _ws(0, _params(ln_eps=0.0), 8, 1024, 128) == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails before any launch
+
+
+def test_attn_fwd_rejects_bad_arguments_before_launch():
+    lib = hs.lib()
+    f = lib.hstu_attn_fwd
+
+    def call(p, B=2, off=FAKE, L=16, T=32, q=FAKE, y=FAKE, ws=FAKE, wsb=0):
+        return f(ctypes.byref(p), B, off, L, T, q, FAKE, FAKE, FAKE, FAKE, y, ws, wsb, None)
+
+    assert call(_params(dtype=3)) == UNSUPPORTED
+    assert call(_params(head_dim=16)) == UNSUPPORTED
+    assert call(_params(num_heads=0)) == INVALID
+    assert call(_params(norm_n=-1)) == INVALID
+    assert call(_params(), B=-1) == INVALID
+    assert call(_params(), q=None) == INVALID
+    assert call(_params(), off=None) == INVALID
+    assert call(_params(), q=FAKE + 4) == INVALID         # misaligned
+    assert call(_params(), ws=None, wsb=1 << 30) == WORKSPACE
+    assert call(_params(), wsb=16) == WORKSPACE           # too small
+    pt = _params(pos_tab=FAKE, n_pos=0)
+    assert call(pt) == INVALID
+    assert call(_params(pos_tab=FAKE, n_pos=4096)) == UNSUPPORTED
+    assert call(_params(time_tab=FAKE, n_time=0)) == INVALID
+    assert call(_params(pos_tab=FAKE, n_pos=128, pos_head_stride=64)) == INVALID
+    # empty work is a no-op that never touches the device
+    assert call(_params(), B=0) == OK
+    assert call(_params(), T=0) == OK
+
+
+def test_cached_and_mfalcon_and_append_reject_bad_arguments():
+    lib = hs.lib()
+    c = hs._KVCache()
+    c.k_pages = c.v_pages = c.ts_pages = c.page_table = FAKE
+    c.num_pages, c.page_size, c.max_pages_per_seq = 10, 64, 4
+    p = _params()
+    r = lib.hstu_attn_fwd_cached(ctypes.byref(p), 2, FAKE, FAKE, 16, 200, 32, FAKE, FAKE, FAKE, ctypes.byref(c),
+                                 FAKE, FAKE, 0, None)
+    assert r == WORKSPACE
+    # max_total beyond what the page table can address
+    r = lib.hstu_attn_fwd_cached(ctypes.byref(p), 2, FAKE, FAKE, 16, 4 * 64 + 1, 32, FAKE, FAKE, FAKE,
+                                 ctypes.byref(c), FAKE, FAKE, 1 << 40, None)
+    assert r == INVALID
+    c.page_size = 32
+    r = lib.hstu_attn_fwd_cached(ctypes.byref(p), 2, FAKE, FAKE, 16, 200, 32, FAKE, FAKE, FAKE, ctypes.byref(c),
+                                 FAKE, FAKE, 1 << 40, None)
+    assert r == UNSUPPORTED
+    assert lib.hstu_kv_append(ctypes.byref(c), ctypes.byref(p), 2, FAKE, FAKE, 32, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    c.page_size = 64
+    assert lib.hstu_kv_append(ctypes.byref(c), ctypes.byref(p), 2, None, FAKE, 32, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.hstu_kv_append(ctypes.byref(c), ctypes.byref(p), 0, FAKE, FAKE, 32, FAKE, FAKE, FAKE, None) == OK
+    r = lib.hstu_mfalcon_fwd(ctypes.byref(p), 2, FAKE, None, 16, 32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             1 << 40, None)
+    assert r == INVALID
+    r = lib.hstu_mfalcon_fwd(ctypes.byref(p), 2, FAKE, FAKE, 16, 32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, None)
+    assert r == WORKSPACE
+
+
+def test_pair_count_matches_closed_forms():
+    assert hs.pair_count("full", [8192] * 8) == 8 * 8192 * 8193 // 2
+    assert hs.pair_count("cached", [128] * 8, [8192] * 8) == 8 * (128 * 8192 + 128 * 129 // 2)
+    assert hs.pair_count("mfalcon", [4096] * 4, [1024] * 4) == 4 * (4096 * 4097 // 2 + 1024 * 4097)
