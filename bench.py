@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Benchmark of the HSTU attention layer on one MI355X.
+
+Headline workload: 8 users x 8,192 tokens, 4 heads x 128, bf16, causal, position
+(128 buckets) + log-time (128 buckets) bias, LayerNorm and U gating. One step
+is one pass of the hot path over that batch: the jagged tile scheduler, the
+fused attention kernel and the LayerNorm/gating epilogue (hstu_attn_fwd),
+with inputs already resident in HBM.
+
+Metric: algorithmic TFLOP/s = 4 * d * H * (allowed query-key pairs) / step
+time, and its fraction of the bf16 dense MFMA peak (2.5 PFLOP/s). The
+attention kernel's own time is measured with HIP events recorded around it on
+the launch stream (roofline.achieved). Other serving variants (KV-cache delta
+with paged append, M-FALCON, the jagged training shape) are reported under
+"variants". The fp64 CPU oracle is timed on a bounded sample of the headline
+workload for reference (cpu_baseline).
+
+Prints exactly one JSON line on stdout.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PMC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_causal_B8_L8192_H4_d128_traffic.json")
+KERNEL_SOURCES = ("attn_fwd.hip", "common.h", "kernels.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "hstu_jagged_silu_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
+    or None when absent or taken on a different kernel source."""
+    try:
+        with open(PMC_FILE) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def timed(fn, steps, warmup, torch, n_events=4):
+    """Run fn(events) warmup times, then `steps` timed times; returns
+    (ms per step over the whole region, list of per-step event tuples)."""
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    import hstu_jagged_silu_amd as hs
+    evs = [[hs.HipEvent() for _ in range(n_events)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        fn(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, evs
+
+
+def mean_span(evs, a, b):
+    return sum(e[a].elapsed_ms(e[b]) for e in evs) / len(evs)
+
+
+def dev(torch, x, dt=None):
+    import numpy as np
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return (t.to(dt) if dt is not None else t).cuda()
+
+
+def bench_full(torch, hs, W, steps, warmup):
+    inp = W.long_seq()
+    bf = torch.bfloat16
+    q, k, v, u = (dev(torch, x, bf) for x in (inp.q, inp.k, inp.v, inp.u))
+    ts, off = dev(torch, inp.ts), dev(torch, inp.seq_offsets)
+    p = hs.LayerParams(num_heads=4, head_dim=128, dtype=bf, pos_tab=dev(torch, inp.tables.pos),
+                       time_tab=dev(torch, inp.tables.time))
+    y = torch.empty_like(u)
+    ws = torch.empty(hs.hstu_workspace_size(hs.HSTU_FN_FULL, p, inp.batch, inp.total, inp.max_len),
+                     dtype=torch.uint8, device="cuda")
+    fn = lambda ev: hs.hstu_attn_fwd(q, k, v, u, ts, off, inp.max_len, p, y=y, workspace=ws, timing_events=ev)
+    ms, evs = timed(fn, steps, warmup, torch)
+    pairs = 4 * hs.pair_count("full", [int(x) for x in inp.lengths])
+    flop = 4 * 128 * pairs
+    return inp, ms, evs, flop
+
+
+def bench_cached(torch, hs, W, steps, warmup):
+    import numpy as np
+    ci = W.kv_cache_delta()
+    h = ci.hist
+    bf = torch.bfloat16
+    p = hs.LayerParams(num_heads=4, head_dim=128, dtype=bf, pos_tab=dev(torch, h.tables.pos),
+                       time_tab=dev(torch, h.tables.time))
+    cache = hs.PagedKVCache.empty(ci.num_pages, 4, 128, dev(torch, ci.page_table), dtype=bf)
+    pre, new = ci.split()
+    hs.hstu_kv_append(cache, dev(torch, ci.prefix_offsets()), dev(torch, np.zeros(ci.batch, np.int32)),
+                      dev(torch, h.k[pre], bf), dev(torch, h.v[pre], bf), dev(torch, h.ts[pre]), p)
+    qn, un, kn, vn = (dev(torch, x[new], bf) for x in (h.q, h.u, h.k, h.v))
+    tsn, noff, cl = dev(torch, h.ts[new]), dev(torch, ci.new_offsets()), dev(torch, ci.cache_lens)
+    max_total = int((ci.cache_lens + ci.new_lens).max())
+    max_new = int(ci.new_lens.max())
+    y = torch.empty_like(un)
+    ws = torch.empty(hs.hstu_workspace_size(hs.HSTU_FN_CACHED, p, ci.batch, len(new), max_total),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(ev):
+        if ev is not None:
+            ev[4].record()
+        hs.hstu_kv_append(cache, noff, cl, kn, vn, tsn, p)
+        hs.hstu_attn_fwd_cached(qn, un, tsn, noff, cl, max_new, max_total, cache, p, y=y, workspace=ws,
+                                timing_events=ev)
+
+    ms, evs = timed(step, steps, warmup, torch, n_events=5)
+    pairs = 4 * hs.pair_count("cached", [int(x) for x in ci.new_lens], [int(x) for x in ci.cache_lens])
+    flop = 4 * 128 * pairs
+    kv_bytes = int(np.sum(ci.cache_lens + ci.new_lens)) * 4 * 128 * 2 * 2
+    attn_ms = mean_span(evs, 1, 2)
+    append_ms = mean_span(evs, 4, 0)
+    return {
+        "workload": ci.name,
+        "ms_per_step": round(ms, 4),
+        "step": "paged append of the new tokens + cached forward (schedule, attention, split reduce + LN/gate)",
+        "attn_kernel_ms": round(attn_ms, 4),
+        "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+        "attn_kernel_tflops": round(flop / (attn_ms * 1e-3) / 1e12, 2),
+        "attn_kernel_kv_gbs": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1),
+        "kv_bytes": kv_bytes,
+        "append_ms": round(append_ms, 4),
+        "epilogue_ms": round(mean_span(evs, 2, 3), 4),
+        "scheduler_ms": round(mean_span(evs, 0, 1), 4),
+        "algorithmic_gflop": round(flop / 1e9, 3),
+    }
+
+
+def bench_mfalcon(torch, hs, W, steps, warmup):
+    ci = W.mfalcon_scoring()
+    inp = ci.inputs
+    bf = torch.bfloat16
+    q, k, v, u = (dev(torch, x, bf) for x in (inp.q, inp.k, inp.v, inp.u))
+    ts, off, nc = dev(torch, inp.ts), dev(torch, inp.seq_offsets), dev(torch, ci.num_candidates)
+    p = hs.LayerParams(num_heads=4, head_dim=128, dtype=bf, pos_tab=dev(torch, inp.tables.pos),
+                       time_tab=dev(torch, inp.tables.time))
+    y = torch.empty_like(u)
+    ws = torch.empty(hs.hstu_workspace_size(hs.HSTU_FN_MFALCON, p, inp.batch, inp.total, inp.max_len),
+                     dtype=torch.uint8, device="cuda")
+    fn = lambda ev: hs.hstu_mfalcon_fwd(q, k, v, u, ts, off, nc, inp.max_len, p, y=y, workspace=ws,
+                                        timing_events=ev)
+    ms, evs = timed(fn, steps, warmup, torch)
+    pairs = 4 * hs.pair_count("mfalcon", [int(x) for x in ci.hist_lens], [int(x) for x in ci.num_candidates])
+    flop = 4 * 128 * pairs
+    naive_pairs = 4 * sum(int(m) * hs.pair_count("full", [int(n) + 1]) for n, m in zip(ci.hist_lens, ci.num_candidates))
+    attn_ms = mean_span(evs, 1, 2)
+    return {
+        "workload": ci.name,
+        "ms_per_step": round(ms, 4),
+        "attn_kernel_ms": round(attn_ms, 4),
+        "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+        "attn_kernel_tflops": round(flop / (attn_ms * 1e-3) / 1e12, 2),
+        "algorithmic_gflop": round(flop / 1e9, 3),
+        "per_candidate_recompute_gflop": round(4 * 128 * naive_pairs / 1e9, 1),
+    }
+
+
+def bench_training_shape(torch, hs, W, steps, warmup):
+    inp = W.training_shape()
+    bf = torch.bfloat16
+    q, k, v, u = (dev(torch, x, bf) for x in (inp.q, inp.k, inp.v, inp.u))
+    ts, off = dev(torch, inp.ts), dev(torch, inp.seq_offsets)
+    p = hs.LayerParams(num_heads=4, head_dim=128, dtype=bf, pos_tab=dev(torch, inp.tables.pos),
+                       time_tab=dev(torch, inp.tables.time))
+    y = torch.empty_like(u)
+    ws = torch.empty(hs.hstu_workspace_size(hs.HSTU_FN_FULL, p, inp.batch, inp.total, inp.max_len),
+                     dtype=torch.uint8, device="cuda")
+    fn = lambda ev: hs.hstu_attn_fwd(q, k, v, u, ts, off, inp.max_len, p, y=y, workspace=ws, timing_events=ev)
+    ms, evs = timed(fn, steps, warmup, torch)
+    flop = 4 * 128 * 4 * hs.pair_count("full", [int(x) for x in inp.lengths])
+    attn_ms = mean_span(evs, 1, 2)
+    return {
+        "workload": inp.name,
+        "total_tokens": inp.total,
+        "ms_per_step": round(ms, 4),
+        "attn_kernel_ms": round(attn_ms, 4),
+        "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+        "attn_kernel_tflops": round(flop / (attn_ms * 1e-3) / 1e12, 2),
+        "algorithmic_gflop": round(flop / 1e9, 3),
+    }
+
+
+def cpu_baseline(inp, rows):
+    """The fp64 oracle on rows 0..rows-1 of user 0 (all heads, N = 8,192): exactly
+    those rows of the headline workload. Returns the cpu_baseline object."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    L = int(inp.lengths[0])
+    sl = slice(0, rows)
+    t0 = time.perf_counter()
+    oracle.hstu_full(inp.q[sl], inp.k[sl], inp.v[sl], inp.u[sl], inp.ts[sl], np.array([0, rows]),
+                     inp.tables.pos, inp.tables.time, norm_n=L)
+    dt = time.perf_counter() - t0
+    flop = 4 * 128 * 4 * rows * (rows + 1) // 2
+    return {
+        "value": round(flop / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"fp64 oracle, user 0 rows 0..{rows - 1} of the 8x8192 workload, 4 heads, N fixed at {L}; "
+                  f"{flop / 1e9:.2f} GFLOP in {dt:.2f} s",
+        "seconds": round(dt, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-variants", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=8192)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU sharding is a design note, not a measured path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hstu_jagged_silu_amd as hs
+    import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    log("headline: 8 x 8192, 4 x 128, bf16")
+    inp, ms, evs, flop = bench_full(torch, hs, W, args.steps, args.warmup)
+    attn_ms = mean_span(evs, 1, 2)
+    sched_ms = mean_span(evs, 0, 1)
+    ln_ms = mean_span(evs, 2, 3)
+    value = flop / (ms * 1e-3) / 1e12
+    achieved = flop / (attn_ms * 1e-3) / 1e12
+    hd = 4 * 128
+    ln_bytes = inp.total * hd * (4 + 2 + 2)   # O fp32 read, U read, Y write (bf16)
+    log(f"step {ms:.4f} ms ({value:.1f} TFLOP/s), attention kernel {attn_ms:.4f} ms ({achieved:.1f} TFLOP/s), "
+        f"scheduler {sched_ms:.4f} ms, epilogue {ln_ms:.4f} ms")
+
+    result = {
+        "metric": "HSTU attention TFLOP/s + % bf16 MFMA peak (1 GPU); ms/layer at seq 8192, d=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "ms_per_layer": round(ms, 4),
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; Q,K,V,U ~ N(0,1), tables ~ N(0,0.02), exponential timestamp gaps mean 60 s)",
+        "config": {"workload": inp.name, "batch": inp.batch, "seq_len": int(inp.lengths[0]), "heads": 4,
+                   "head_dim": 128, "rab": "position 128 + log2 time 128 buckets", "mask": "causal",
+                   "algorithmic_gflop": round(flop / 1e9, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                     "kernel": "attn_fwd_kernel<bf16,128,full>", "kernel_ms": round(attn_ms, 4)},
+        "kernels_ms": {"scheduler": round(sched_ms, 4), "attention": round(attn_ms, 4),
+                       "ln_gate": round(ln_ms, 4)},
+        "epilogue": {"bound": "hbm", "achieved_gbs": round(ln_bytes / (ln_ms * 1e-3) / 1e9, 1),
+                     "peak_gbs": PEAK_HBM_GBS, "bytes": ln_bytes},
+    }
+    if not args.no_variants:
+        variants = {}
+        for name, fn in (("kv_cache_delta", bench_cached), ("mfalcon", bench_mfalcon),
+                         ("jagged_training_shape", bench_training_shape)):
+            log(f"variant {name}")
+            variants[name] = fn(torch, hs, W, args.steps, args.warmup)
+            log(f"  {variants[name]}")
+        result["variants"] = variants
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_sample_rows} rows")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_rows)
+        log(f"  {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -47,7 +47,7 @@ class _Params(ctypes.Structure):
         ("pos_tab", ctypes.c_void_p), ("n_pos", ctypes.c_int32), ("pos_head_stride", ctypes.c_int32),
         ("time_tab", ctypes.c_void_p), ("n_time", ctypes.c_int32), ("time_head_stride", ctypes.c_int32),
         ("ln_w", ctypes.c_void_p), ("ln_b", ctypes.c_void_p), ("ln_eps", ctypes.c_float),
-        ("timing_events", ctypes.c_void_p * 2),
+        ("timing_events", ctypes.c_void_p * 4),
     ]
 
 
@@ -159,8 +159,8 @@ class LayerParams:
             setattr(p, name, None if t is None else t.data_ptr())
         p.ln_eps = self.ln_eps
         if timing_events is not None:
-            p.timing_events[0] = timing_events[0].cuda_event
-            p.timing_events[1] = timing_events[1].cuda_event
+            for i, ev in enumerate(timing_events[:4]):
+                p.timing_events[i] = None if ev is None else ev.cuda_event
         return p
 
 
@@ -330,6 +330,40 @@ def hstu_attn_fwd_cached(q_new, u_new, ts_new, new_offsets, cache_lens, max_new:
                                      ctypes.byref(c), y.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
            "hstu_attn_fwd_cached")
     return y
+
+
+class HipEvent:
+    """A raw HIP event for the library's timing_events slots (torch's Event
+    refuses elapsed times of events it did not record itself)."""
+    _hip = None
+
+    def __init__(self):
+        if HipEvent._hip is None:
+            h = ctypes.CDLL("libamdhip64.so")
+            h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            HipEvent._hip = h
+        ev = ctypes.c_void_p()
+        if HipEvent._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise HstuError("hipEventCreate failed")
+        self.cuda_event = ev.value
+
+    def record(self):
+        if HipEvent._hip.hipEventRecord(self.cuda_event, _stream()) != 0:
+            raise HstuError("hipEventRecord failed")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        if HipEvent._hip.hipEventElapsedTime(ctypes.byref(ms), self.cuda_event, end.cuda_event) != 0:
+            raise HstuError("hipEventElapsedTime failed (events not recorded or not complete)")
+        return float(ms.value)
+
+    def __del__(self):
+        if self.cuda_event and HipEvent._hip is not None:
+            HipEvent._hip.hipEventDestroy(self.cuda_event)
+            self.cuda_event = None
 
 
 def pair_count(kind: str, lengths: Sequence[int], extra: Optional[Sequence[int]] = None) -> int:

@@ -3,6 +3,7 @@
 // synchronisation; everything is queued on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 
@@ -68,8 +69,10 @@ bool layout(int fn, const hstu_params_t* p, int32_t B, int64_t Tq, int64_t max_l
   } else if (fn == HSTU_FN_MFALCON) {
     w.max_items = H * (tiles + B);
   } else if (fn == HSTU_FN_CACHED) {
+    // splits actually used are ceil(max_len / chunk_keys) <= this bound, which
+    // never decreases when max_len grows
     w.chunk_keys = chunk_keys_for(max_len);
-    w.n_chunks = (int32_t)(max_len > 0 ? ceil_div(max_len, w.chunk_keys) : 1);
+    w.n_chunks = (int32_t)std::min<int64_t>(MAX_SPLITS, std::max<int64_t>(1, ceil_div(max_len, 8 * KT)));
     w.max_items = H * tiles * w.n_chunks;
   } else {
     return false;
@@ -135,12 +138,15 @@ LnArgs ln_args(const hstu_params_t* p, const WsLayout& w, void* ws, const void* 
 
 hstu_status_t run_attention(const hstu_params_t* p, const SchedArgs& s, const AttnArgs& a, int mode,
                             const LnArgs& l, hipStream_t stream) {
-  if (launch_sched(s, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
-  hipEvent_t ev0 = (hipEvent_t)p->timing_events[0], ev1 = (hipEvent_t)p->timing_events[1];
-  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
-  if (launch_attn(a, p->dtype, p->head_dim, mode, s.max_items, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
-  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
-  if (launch_ln_gate(l, p->dtype, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  auto mark = [&](int i) {
+    hipEvent_t ev = (hipEvent_t)p->timing_events[i];
+    return !ev || hipEventRecord(ev, stream) == hipSuccess;
+  };
+  if (!mark(0) || launch_sched(s, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  if (!mark(1) || launch_attn(a, p->dtype, p->head_dim, mode, s.max_items, stream) != hipSuccess)
+    return HSTU_ERR_LAUNCH;
+  if (!mark(2) || launch_ln_gate(l, p->dtype, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  if (!mark(3)) return HSTU_ERR_LAUNCH;
   return HSTU_OK;
 }
 

@@ -96,7 +96,8 @@ template <int NB> __device__ inline void store_bytes(unsigned char* p, const uns
 }
 
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NTHREADS, (sizeof(T) == 4 && D == 128) ? 1 : 2)  // fp32 d=128: LDS allows one
+void attn_fwd_kernel(AttnArgs a) {
   using G = Geo<T, D>;
   using M = Mfma<T>;
   __shared__ Smem<T, D> sm;

@@ -88,9 +88,11 @@ typedef enum { HSTU_FN_FULL = 0, HSTU_FN_CACHED = 1, HSTU_FN_MFALCON = 2 } hstu_
  *                 beyond index 63 are unreachable for int64 seconds).
  *   ln_w, ln_b    NULL for 1 / 0, else fp32 [H*d] affine terms of the norm.
  *   ln_eps        LayerNorm epsilon (1e-5 in the plain reading), > 0.
- *   timing_events optional pair of hipEvent_t (cast to void*) recorded on the
- *                 stream immediately before and after the fused attention
- *                 kernel, for timing that kernel alone; NULL to skip.
+ *   timing_events optional hipEvent_t handles (cast to void*), each NULL to
+ *                 skip, recorded on the stream: [0] before the tile scheduler,
+ *                 [1] before the fused attention kernel, [2] after it, [3]
+ *                 after the LayerNorm/gating epilogue. For timing the kernels
+ *                 of one call separately; the library never waits on them.
  */
 typedef struct {
   int32_t num_heads;
@@ -107,7 +109,7 @@ typedef struct {
   const float* ln_w;
   const float* ln_b;
   float ln_eps;
-  void* timing_events[2];
+  void* timing_events[4];
 } hstu_params_t;
 
 /*
@@ -144,9 +146,9 @@ int32_t hstu_version(void);
  *   total_q_tokens  query rows T (full, M-FALCON) or new rows (cached)
  *   max_len         longest user: L (full), history + candidates (M-FALCON),
  *                   cache_len + new tokens (cached)
- * Returns 0 when the arguments are invalid. The value depends only on the
- * arguments, so a workspace sized once for the largest call serves all
- * smaller ones.
+ * Returns 0 when the arguments are invalid. The value depends only on these
+ * arguments and never decreases when one of them grows, so a workspace sized
+ * once for the largest call serves every smaller one.
  */
 size_t hstu_workspace_size(int32_t fn, const hstu_params_t* params, int32_t batch,
                            int64_t total_q_tokens, int32_t max_len);
