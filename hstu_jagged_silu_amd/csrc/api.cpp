@@ -64,6 +64,8 @@ bool layout(int fn, const hstu_params_t* p, int32_t B, int64_t Tq, int64_t max_l
   const int64_t tiles = ceil_div(Tq, QT) + B;  // bound on sum_b ceil(L_b / QT)
   w.n_chunks = 1;
   w.chunk_keys = 0;
+  w.stat_stride = 0;
+  w.n_stat_blocks = ceil_div(Tq, KT);           // jagged keys: packed 64-row blocks
   if (fn == HSTU_FN_FULL) {
     w.max_items = H * tiles;
   } else if (fn == HSTU_FN_MFALCON) {
@@ -74,13 +76,16 @@ bool layout(int fn, const hstu_params_t* p, int32_t B, int64_t Tq, int64_t max_l
     w.chunk_keys = chunk_keys_for(max_len);
     w.n_chunks = (int32_t)std::min<int64_t>(MAX_SPLITS, std::max<int64_t>(1, ceil_div(max_len, 8 * KT)));
     w.max_items = H * tiles * w.n_chunks;
+    w.stat_stride = (int32_t)std::max<int64_t>(1, ceil_div(max_len, KT));
+    w.n_stat_blocks = (int64_t)B * w.stat_stride;
   } else {
     return false;
   }
   if (w.max_items > INT_MAX / 2) return false;
   w.items_off = ALIGN;
   w.scratch_off = align_up(w.items_off + (size_t)w.max_items * sizeof(WorkItem));
-  w.o_off = align_up(w.scratch_off + (size_t)(B + 1) * sizeof(int32_t));
+  w.stats_off = align_up(w.scratch_off + (size_t)(B + 1) * sizeof(int32_t));
+  w.o_off = align_up(w.stats_off + (size_t)w.n_stat_blocks * 2 * sizeof(int64_t));
   w.total = align_up(w.o_off + (size_t)w.n_chunks * (size_t)Tq * (size_t)HD * sizeof(float));
   return true;
 }
@@ -102,6 +107,9 @@ AttnArgs base_args(const hstu_params_t* p, const WsLayout& w, void* ws, int64_t 
   a.o = (float*)((char*)ws + w.o_off);
   a.o_chunk_stride = Tq * (int64_t)p->num_heads * p->head_dim;
   a.n_chunks = w.n_chunks;
+  a.tstats = (const int64_t*)((char*)ws + w.stats_off);
+  a.n_stat_blocks = w.n_stat_blocks;
+  a.stat_stride = w.stat_stride;
   return a;
 }
 
@@ -118,6 +126,10 @@ SchedArgs sched_args(int mode, const hstu_params_t* p, const WsLayout& w, void* 
   s.prefix = (int32_t*)((char*)ws + w.scratch_off);
   s.items = (WorkItem*)((char*)ws + w.items_off);
   s.count = (int32_t*)ws;
+  s.tstats = (int64_t*)((char*)ws + w.stats_off);
+  s.stat_stride = w.stat_stride;
+  // ranges are only needed when a time table is present
+  s.n_stat_blocks = p->time_tab ? w.n_stat_blocks : 0;
   return s;
 }
 
@@ -202,6 +214,8 @@ hstu_status_t hstu_attn_fwd(const hstu_params_t* params, int32_t batch, const in
   if (!ws || ws_bytes < w.total || !aligned16(ws)) return HSTU_ERR_WORKSPACE;
 
   SchedArgs s = sched_args(MODE_FULL, params, w, ws, batch, seq_offsets, max_len);
+  s.ts = ts;
+  s.Tk = total_tokens;
   AttnArgs a = base_args(params, w, ws, total_tokens);
   a.q = q;
   a.k = k;
@@ -228,6 +242,8 @@ hstu_status_t hstu_mfalcon_fwd(const hstu_params_t* params, int32_t batch, const
 
   SchedArgs s = sched_args(MODE_MFALCON, params, w, ws, batch, seq_offsets, max_len);
   s.num_cand = num_candidates;
+  s.ts = ts;
+  s.Tk = total_tokens;
   AttnArgs a = base_args(params, w, ws, total_tokens);
   a.q = q;
   a.k = k;
@@ -247,7 +263,7 @@ hstu_status_t hstu_kv_append(const hstu_kv_cache_t* cache, const hstu_params_t* 
   if (st != HSTU_OK) return st;
   if (!cache) return HSTU_ERR_INVALID_ARG;
   if (cache->page_size != PAGE) return HSTU_ERR_UNSUPPORTED;
-  if (batch < 0 || total_new < 0 || cache->num_pages < 0 || cache->max_pages_per_seq < 0)
+  if (batch < 0 || total_new < 0 || cache->num_pages < 1 || cache->max_pages_per_seq < 1)
     return HSTU_ERR_INVALID_ARG;
   if (batch == 0 || total_new == 0) return HSTU_OK;
   if (any_null({cache->k_pages, cache->v_pages, cache->ts_pages, cache->page_table, new_offsets, cache_lens,
@@ -284,8 +300,8 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_params_t* params, int32_t batch, c
   if (st != HSTU_OK) return st;
   if (!cache) return HSTU_ERR_INVALID_ARG;
   if (cache->page_size != PAGE) return HSTU_ERR_UNSUPPORTED;
-  if (batch < 0 || total_new < 0 || max_new < 0 || max_total < 0 || cache->num_pages < 0 ||
-      cache->max_pages_per_seq < 0)
+  if (batch < 0 || total_new < 0 || max_new < 0 || max_total < 0 || cache->num_pages < 1 ||
+      cache->max_pages_per_seq < 1)
     return HSTU_ERR_INVALID_ARG;
   if (batch == 0 || total_new == 0) return HSTU_OK;
   if (any_null({cache->k_pages, cache->v_pages, cache->ts_pages, cache->page_table, new_offsets, cache_lens,
@@ -300,6 +316,10 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_params_t* params, int32_t batch, c
 
   SchedArgs s = sched_args(MODE_CACHED, params, w, ws, batch, new_offsets, w.chunk_keys);
   s.cache_lens = cache_lens;
+  s.ts_pages = cache->ts_pages;
+  s.page_table = cache->page_table;
+  s.num_pages = cache->num_pages;
+  s.max_pages = cache->max_pages_per_seq;
   AttnArgs a = base_args(params, w, ws, total_new);
   a.q = q_new;
   a.ts = ts_new;

@@ -12,6 +12,10 @@
 // GPU Cloud", section "M-FALCON: Microbatched Attention ...".
 //
 // Data flow inside one wave (32 query rows, one 64-key tile):
+//   * K and V tiles go from HBM straight into LDS (global_load_lds, 16 bytes
+//     per lane), row-major with an XOR swizzle on 16-byte chunks chosen by
+//     which global chunk each lane fetches. No registers hold the prefetch;
+//     the next tile streams in while the current one is computed.
 //   * The score tile is computed transposed, S^T[key][q] = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (fp32: v_mfma_f32_32x32x2_f32). The 32x32
 //     accumulator puts query q = lane % 32 in every register of a lane, and
@@ -19,10 +23,9 @@
 //   * K rows are fed to the MFMA in a permuted order so that, after SiLU, the
 //     8 consecutive accumulator registers of a lane hold 8 consecutive keys:
 //     they are exactly the B operand (P^T) of the second product
-//     O^T[d][q] += V^T[d][key] P^T[key][q]. No shuffle or LDS round trip sits
-//     between the two products.
-//   * V is stored transposed in LDS (V^T[d][key]) while it is staged, so the
-//     A operand of the second product is one 16-byte LDS read.
+//     O^T[d][q] += V^T[d][key] P^T[key][q]. No shuffle sits between the two.
+//   * The A operand V^T of the second product is read from the row-major V
+//     tile with two transposing LDS reads (ds_read_b64_tr_b16).
 //   * The bias is folded into one FMA per score: y = s * (-alpha log2 e) + b'
 //     with b' = -log2(e) (P[.] + T[.]); then SiLU(x) = -ln2 * y / (1 + 2^y),
 //     and the -ln2 / N factor moves to the epilogue. Far from the diagonal a
@@ -31,6 +34,9 @@
 #include "kernels.h"
 
 namespace hstu {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 template <typename T> struct Mfma;
 
@@ -60,26 +66,34 @@ template <> struct Mfma<float> {
   __device__ static inline int krow(int kb, int r) { return kb * 32 + r; }
 };
 
-// LDS geometry of one key tile for element type T and head dim D.
+// LDS geometry of one key tile (KT rows of D elements) for element type T.
 template <typename T, int D> struct Geo {
   static constexpr int EPC = 16 / sizeof(T);            // elements per 16-byte chunk
-  static constexpr int KCPR = D / EPC;                  // chunks per K row (one key)
-  static constexpr int VCPR = KT / EPC;                 // chunks per V^T row (one d)
-  static constexpr int KPT = KCPR * KT / NTHREADS;      // keys staged per thread
-  static constexpr int TILE = KT * D * (int)sizeof(T);  // bytes of one K (or V) tile
+  static constexpr int CPR = D / EPC;                   // chunks per row (one key)
+  static constexpr int ROWB = D * (int)sizeof(T);       // bytes per row
+  static constexpr int TILE = KT * ROWB;                // bytes of one K (or V) tile
+  static constexpr int NDMA = TILE / (NWAVES * 1024);   // 1 KB LDS DMA instructions per wave
   static constexpr int NDB = D / 32;                    // 32-wide d blocks of O
-  static constexpr int NQOP = D / Mfma<T>::KS;          // Q operands per lane
-  static_assert(KPT >= 1 && KCPR * (KT / KPT) == NTHREADS, "staging map");
-  // XOR swizzles on 16-byte chunks keep the MFMA operand reads conflict-free
-  __device__ static inline int k_off(int r, int c) { return (r * KCPR + (c ^ (r % KCPR))) * 16; }
-  __device__ static inline int v_off(int d, int c) { return (d * VCPR + (c ^ ((d ^ (d / VCPR)) % VCPR))) * 16; }
+  static constexpr int NQOP = D / Mfma<T>::KS;          // Q (and K) operands per lane per key block
+  static_assert(NDMA >= 1 && NDMA * NWAVES * 1024 == TILE, "tile staging map");
+  // XOR swizzles on 16-byte chunks. K: MFMA operand reads (8 lanes, 8 rows,
+  // one chunk) hit distinct chunks. V (bf16): the transposing reads (16
+  // lanes: 4 consecutive rows x 2 adjacent chunks) hit 8 distinct chunks.
+  __device__ static inline int swz_k(int r) { return r % CPR; }
+  __device__ static inline int swz_v(int r) { return sizeof(T) == 2 ? (2 * r) % CPR : r % CPR; }
+  __device__ static inline int k_off(int r, int c) { return r * ROWB + ((c ^ swz_k(r)) << 4); }
+  __device__ static inline int v_off(int r, int c) { return r * ROWB + ((c ^ swz_v(r)) << 4); }
 };
 
-template <typename T, int D> struct Smem {
-  unsigned char kv[2][2][Geo<T, D>::TILE] __attribute__((aligned(16)));  // [buffer][K, V^T]
-  int32_t ts_lo[2][KT];
-  int64_t ts64[2][KT];
-  int64_t ts_mm[2][2];
+// One pipeline stage: a K tile, a V tile and the keys' timestamps.
+template <typename T, int D> struct Stage {
+  unsigned char k[Geo<T, D>::TILE] __attribute__((aligned(16)));
+  unsigned char v[Geo<T, D>::TILE] __attribute__((aligned(16)));
+  int32_t ts_lo[KT];
+  int64_t ts64[KT];
+};
+
+struct Tables {
   float pos_t[MAX_NPOS];   // -log2(e) * position table
   float time_t[64];        // -log2(e) * time table, indexed by clz64(|dt| + 1)
 };
@@ -88,11 +102,29 @@ __device__ inline int64_t shfl_xor64(int64_t x, int m) {
   return (int64_t)__shfl_xor((long long)x, m);
 }
 
-template <int NB> __device__ inline void store_bytes(unsigned char* p, const unsigned char* src) {
-  if constexpr (NB == 16) *(i32x4*)p = *(const i32x4*)src;
-  else if constexpr (NB == 8) *(uint64_t*)p = *(const uint64_t*)src;
-  else if constexpr (NB == 4) *(uint32_t*)p = *(const uint32_t*)src;
-  else *(uint16_t*)p = *(const uint16_t*)src;
+// Read-only data at a wave-uniform address through the constant address
+// space: the compiler then emits a scalar load, whose wait does not also wait
+// for the vector-memory DMA that is streaming the next key tile.
+template <typename V> __device__ inline V ldc(const V* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if constexpr (sizeof(V) % 4 == 0 && sizeof(V) > 8) {  // structs: copy word by word
+    V out;
+    const __attribute__((address_space(4))) uint32_t* q = (const __attribute__((address_space(4))) uint32_t*)(uintptr_t)p;
+    uint32_t* o = (uint32_t*)&out;
+    #pragma unroll
+    for (int i = 0; i < (int)(sizeof(V) / 4); ++i) o[i] = q[i];
+    return out;
+  } else {
+    return *(const __attribute__((address_space(4))) V*)(uintptr_t)p;
+  }
+#else
+  return *p;  // host pass of the kernel template (never executed)
+#endif
+}
+
+__device__ inline int64_t uniform64(int64_t x) {
+  return (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)x) |
+         ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32)) << 32);
 }
 
 template <typename T, int D, int MODE>
@@ -100,29 +132,35 @@ __global__ __launch_bounds__(NTHREADS, (sizeof(T) == 4 && D == 128) ? 1 : 2)  //
 void attn_fwd_kernel(AttnArgs a) {
   using G = Geo<T, D>;
   using M = Mfma<T>;
-  __shared__ Smem<T, D> sm;
+  // Two distinct LDS objects (not one array indexed by stage): the compiler
+  // can then tell that reads of one stage never alias the DMA into the other
+  // and does not wait for the prefetch before every operand read.
+  __shared__ Stage<T, D> st0;
+  __shared__ Stage<T, D> st1;
+  __shared__ Tables tab;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, hl = lane >> 5, l32 = lane & 31;
-  if ((int64_t)blockIdx.x >= (int64_t)*a.count) return;
-  const WorkItem it = a.items[blockIdx.x];
+  const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave facts in SGPRs
+  if ((int64_t)blockIdx.x >= (int64_t)ldc(a.count)) return;
+  const WorkItem it = ldc(a.items + blockIdx.x);
   const int b = it.b, h = it.h, kind = it.kind;
   const int q_start = it.q_start, q_len = it.q_len;
   const int k_begin = it.k_begin, k_end = it.k_end;
   const int H = a.H;
 
   // ---- per-user geometry -------------------------------------------------
-  const int64_t q_off = a.offsets[b];
-  const int Lq = a.offsets[b + 1] - (int)q_off;
+  const int64_t q_off = ldc(a.offsets + b);
+  const int Lq = ldc(a.offsets + b + 1) - (int)q_off;
   int kcount, pos0, n_norm;
   bool cand = false;
   if (MODE == MODE_CACHED) {
-    const int C = a.cache_lens[b];
+    const int C = ldc(a.cache_lens + b);
     kcount = C + Lq;
     pos0 = C + q_start;
     n_norm = C + Lq;
   } else if (MODE == MODE_MFALCON) {
-    const int n = Lq - a.num_cand[b];
+    const int n = Lq - ldc(a.num_cand + b);
     kcount = n;
     cand = (kind == KIND_CANDIDATE);
     pos0 = cand ? n : q_start;
@@ -138,14 +176,14 @@ void attn_fwd_kernel(AttnArgs a) {
   const int n_pos = a.pos_tab ? a.n_pos : 1;
   {
     const float* pt = a.pos_tab ? a.pos_tab + (int64_t)h * a.pos_stride : nullptr;
-    for (int i = tid; i < n_pos; i += NTHREADS) sm.pos_t[i] = pt ? pt[i] * -LOG2E : 0.0f;
+    for (int i = tid; i < n_pos; i += NTHREADS) tab.pos_t[i] = pt ? pt[i] * -LOG2E : 0.0f;
     if (tid < 64) {
       float t = 0.0f;
       if (a.time_tab) {
         int bk = min(63 - tid, a.n_time - 1);
         t = a.time_tab[(int64_t)h * a.time_stride + bk] * -LOG2E;
       }
-      sm.time_t[tid] = t;
+      tab.time_t[tid] = t;
     }
   }
 
@@ -170,6 +208,8 @@ void attn_fwd_kernel(AttnArgs a) {
     w_ts_min = min(w_ts_min, shfl_xor64(w_ts_min, m));
     w_ts_max = max(w_ts_max, shfl_xor64(w_ts_max, m));
   }
+  w_ts_min = uniform64(w_ts_min);
+  w_ts_max = uniform64(w_ts_max);
 
   // ---- Q operands in registers ---------------------------------------------
   typename M::op qop[G::NQOP];
@@ -188,86 +228,86 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   }
 
-  // ---- key tile staging -----------------------------------------------------
-  const int dchunk = tid % G::KCPR, kgroup = tid / G::KCPR;
-  i32x4 kreg[G::KPT], vreg[G::KPT];
+  // ---- key tile staging (HBM -> LDS, no registers) --------------------------
+  // Keys past the end of a user (partial last tile) read a copy of the last
+  // valid row: finite values that the causal mask zeroes. A missing page of
+  // the cached path reads as zeros.
   int64_t tsreg = 0;
 
-  auto load_tile = [&](int j0) {
-    const T* kbase = nullptr;
-    const T* vbase = nullptr;
-    int64_t rstride = 0;
-    const int64_t* tsbase = nullptr;
-    int64_t kmax_rows = KT;   // rows readable from kbase
+  auto issue_tile = [&](Stage<T, D>& st, int j0) {
+    const unsigned char* kbase;
+    const unsigned char* vbase;
+    const int64_t* tsbase;
+    int64_t rstride;  // bytes between consecutive keys
+    int nvalid = min(KT, kcount - j0);
+    bool missing = false;
     if (MODE == MODE_CACHED) {
-      const int page = j0 / PAGE < a.max_pages ? a.page_table[(int64_t)b * a.max_pages + j0 / PAGE] : -1;
-      if (page >= 0 && page < a.num_pages) {
-        const int64_t pb = ((int64_t)page * H + h) * PAGE * D;
-        kbase = (const T*)a.k_pages + pb;
-        vbase = (const T*)a.v_pages + pb;
-        rstride = D;
-        tsbase = a.ts_pages + (int64_t)page * PAGE;
+      int page = j0 / PAGE < a.max_pages ? ldc(a.page_table + (int64_t)b * a.max_pages + j0 / PAGE) : -1;
+      if (page < 0 || page >= a.num_pages) {
+        page = 0;
+        missing = true;
+      }
+      const int64_t pb = (((int64_t)page * H + h) * PAGE * D) * (int64_t)sizeof(T);
+      kbase = (const unsigned char*)a.k_pages + pb;
+      vbase = (const unsigned char*)a.v_pages + pb;
+      rstride = G::ROWB;
+      tsbase = a.ts_pages + (int64_t)page * PAGE;
+    } else {
+      const int64_t r0 = min(q_off + j0, a.Tq - 1);
+      nvalid = (int)min<int64_t>(nvalid, a.Tq - r0);
+      kbase = (const unsigned char*)a.k + ((r0 * H + h) * D) * (int64_t)sizeof(T);
+      vbase = (const unsigned char*)a.v + ((r0 * H + h) * D) * (int64_t)sizeof(T);
+      rstride = (int64_t)H * G::ROWB;
+      tsbase = a.ts + r0;
+    }
+    const int last = max(nvalid - 1, 0);
+    if (missing) {
+      #pragma unroll
+      for (int i = 0; i < G::NDMA; ++i) {
+        const int P = (wave * G::NDMA + i) * 64 + lane;  // 16-byte LDS chunk this lane fills
+        *(i32x4*)(st.k + P * 16) = i32x4{};
+        *(i32x4*)(st.v + P * 16) = i32x4{};
       }
     } else {
-      if (q_off + j0 < a.Tq) {
-        kbase = (const T*)a.k + ((q_off + j0) * H + h) * D;
-        vbase = (const T*)a.v + ((q_off + j0) * H + h) * D;
-        rstride = (int64_t)H * D;
-        tsbase = a.ts + q_off + j0;
-        kmax_rows = a.Tq - (q_off + j0);
+      #pragma unroll
+      for (int i = 0; i < G::NDMA; ++i) {
+        const int base = (wave * G::NDMA + i) * 64;      // first LDS chunk of this instruction
+        const int P = base + lane;
+        const int r = P / G::CPR, pc = P % G::CPR;
+        const int64_t row = min(r, last) * rstride;
+        __builtin_amdgcn_global_load_lds((const void*)(kbase + row + ((pc ^ G::swz_k(r)) << 4)),
+                                         LDS_PTR(void, st.k + base * 16), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vbase + row + ((pc ^ G::swz_v(r)) << 4)),
+                                         LDS_PTR(void, st.v + base * 16), 16, 0, 0);
       }
     }
-    #pragma unroll
-    for (int i = 0; i < G::KPT; ++i) {
-      const int kl = kgroup * G::KPT + i;
-      if (kbase && j0 + kl < kcount && kl < kmax_rows) {
-        kreg[i] = *(const i32x4*)(kbase + kl * rstride + dchunk * G::EPC);
-        vreg[i] = *(const i32x4*)(vbase + kl * rstride + dchunk * G::EPC);
-      } else {
-        kreg[i] = i32x4{};
-        vreg[i] = i32x4{};
-      }
-    }
-    if (wave == 0) {
-      const bool ok = tsbase && j0 + lane < kcount && lane < kmax_rows;
-      tsreg = ok ? tsbase[lane] : 0;
-    }
+    if (wave == 0) tsreg = tsbase[min(lane, last)];
   };
 
-  auto store_tile = [&](int buf, int j0) {
-    unsigned char* kl = sm.kv[buf][0];
-    unsigned char* vl = sm.kv[buf][1];
-    #pragma unroll
-    for (int i = 0; i < G::KPT; ++i) *(i32x4*)(kl + G::k_off(kgroup * G::KPT + i, dchunk)) = kreg[i];
-    // transpose: V^T[d][keys kgroup*KPT ...] for every d of this thread's chunk
-    constexpr int PIECE = G::KPT < G::EPC ? G::KPT : G::EPC;  // keys per LDS store
-    #pragma unroll
-    for (int e = 0; e < G::EPC; ++e) {
-      const int d = dchunk * G::EPC + e;
-      #pragma unroll
-      for (int i0 = 0; i0 < G::KPT; i0 += PIECE) {
-        T vals[PIECE];
-        #pragma unroll
-        for (int i = 0; i < PIECE; ++i) vals[i] = ((const T*)&vreg[i0 + i])[e];
-        const int key = kgroup * G::KPT + i0;
-        store_bytes<PIECE * (int)sizeof(T)>(vl + G::v_off(d, key / G::EPC) + (key % G::EPC) * sizeof(T),
-                                            (const unsigned char*)vals);
-      }
-    }
+  // Wait for this wave's DMA, publish the timestamps, then the barrier makes
+  // the whole tile visible to every wave.
+  auto finish_tile = [&](Stage<T, D>& st) {
+    __builtin_amdgcn_s_waitcnt(0);
     if (wave == 0) {
-      const bool ok = j0 + lane < kcount;
-      sm.ts_lo[buf][lane] = (int32_t)tsreg;
-      sm.ts64[buf][lane] = tsreg;
-      int64_t mn = ok ? tsreg : INT64_MAX, mx = ok ? tsreg : INT64_MIN;
-      for (int m = 32; m >= 1; m >>= 1) {
-        mn = min(mn, shfl_xor64(mn, m));
-        mx = max(mx, shfl_xor64(mx, m));
-      }
-      if (lane == 0) {
-        sm.ts_mm[buf][0] = mn;
-        sm.ts_mm[buf][1] = mx;
-      }
+      st.ts_lo[lane] = (int32_t)tsreg;
+      st.ts64[lane] = tsreg;
     }
+    __syncthreads();
+  };
+
+  // timestamp range of the keys of the tile at j0 (conservative superset)
+  auto key_time_range = [&](int j0, int64_t& kmin, int64_t& kmax) {
+    if (MODE == MODE_CACHED) {
+      const int64_t blk = (int64_t)b * a.stat_stride + j0 / KT;
+      kmin = ldc(a.tstats + 2 * blk);
+      kmax = ldc(a.tstats + 2 * blk + 1);
+    } else {
+      const int64_t r0 = q_off + j0;
+      const int64_t i0 = min(r0 / KT, a.n_stat_blocks - 1), i1 = min((r0 + KT - 1) / KT, a.n_stat_blocks - 1);
+      kmin = min(ldc(a.tstats + 2 * i0), ldc(a.tstats + 2 * i1));
+      kmax = max(ldc(a.tstats + 2 * i0 + 1), ldc(a.tstats + 2 * i1 + 1));
+    }
+    if (kmin > kmax) kmin = kmax = w_ts_min;  // no valid key: the bias value is irrelevant
   };
 
   // ---- accumulators -------------------------------------------------------
@@ -279,14 +319,23 @@ void attn_fwd_kernel(AttnArgs a) {
   const bool has_time = a.time_tab != nullptr;
   const int n_time_eff = a.time_tab ? min(a.n_time, 64) : 1;
 
-  auto compute_tile = [&](int buf, int j0) {
+  // source address of this lane for the transposing V read of operand (db, c), half s4
+  const int tr_g = lane >> 4, tr_j = lane & 15;
+  auto v_tr_off = [&](int db, int c, int s4) {
+    const int key = 16 * c + 8 * (tr_g >> 1) + 4 * s4 + (tr_j >> 2);
+    const int d = 32 * db + 16 * (tr_g & 1) + 4 * (tr_j & 3);
+    return G::v_off(key, d / G::EPC) + (d % G::EPC) * (int)sizeof(T);
+  };
+
+  auto compute_tile = [&](Stage<T, D>& st, int j0) {
     if (!w_rows || j0 > w_lim_max) return;  // every pair of this wave masked
-    const unsigned char* kl = sm.kv[buf][0];
-    const unsigned char* vl = sm.kv[buf][1];
+    const unsigned char* kl = st.k;
+    const unsigned char* vl = st.v;
 
     // classify the wave tile: mask, constant bias, or per-element bias
     const bool need_mask = j0 + KT - 1 > w_lim_min;
-    const int64_t k_min = sm.ts_mm[buf][0], k_max = sm.ts_mm[buf][1];
+    int64_t k_min = 0, k_max = 0;
+    if (has_time) key_time_range(j0, k_min, k_max);
     const bool pos_uniform = (a.pos_tab == nullptr) || (w_p_min - (j0 + KT - 1) >= n_pos - 1);
     bool time_uniform = !has_time;
     float c_time = 0.0f;
@@ -301,11 +350,11 @@ void attn_fwd_kernel(AttnArgs a) {
       if (ordered) {
         const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
         const int blo = min(63 - zlo, n_time_eff - 1), bhi = min(63 - zhi, n_time_eff - 1);
-        if (blo == bhi) { time_uniform = true; c_time = sm.time_t[zlo]; }
+        if (blo == bhi) { time_uniform = true; c_time = tab.time_t[zlo]; }
       }
     }
     const bool uniform = pos_uniform && time_uniform;
-    const float cb_uniform = sm.pos_t[n_pos - 1] * (a.pos_tab ? 1.0f : 0.0f) + c_time;
+    const float cb_uniform = tab.pos_t[n_pos - 1] * (a.pos_tab ? 1.0f : 0.0f) + c_time;
     const bool small_span = span_hi < ((int64_t)1 << 31) - 2;
     const int32_t tsq_lo = (int32_t)tsq;
     const int lim_rel = lim_lane - j0;
@@ -313,18 +362,20 @@ void attn_fwd_kernel(AttnArgs a) {
     // one 32-key block at a time: S^T = K Q^T, SiLU, O^T += V^T P^T
     #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 acc = f32x16{};
+      typename M::op kop[G::NQOP];
+      const int kr = M::krow(kb, l32);
       #pragma unroll
       for (int s = 0; s < G::NQOP; ++s) {
-        typename M::op kop;
         if constexpr (sizeof(T) == 2) {
-          kop = *(const bf16x8*)(kl + G::k_off(M::krow(kb, l32), 2 * s + hl));
+          kop[s] = *(const bf16x8*)(kl + G::k_off(kr, 2 * s + hl));
         } else {
           const int d = 2 * s + hl;
-          kop = *(const float*)(kl + G::k_off(M::krow(kb, l32), d / 4) + (d % 4) * 4);
+          kop[s] = *(const float*)(kl + G::k_off(kr, d / 4) + (d % 4) * 4);
         }
-        acc = M::run(kop, qop[s], acc);
       }
+      f32x16 acc = f32x16{};
+      #pragma unroll
+      for (int s = 0; s < G::NQOP; ++s) acc = M::run(kop[s], qop[s], acc);
 
       float p[16];
       if (uniform) {
@@ -335,25 +386,32 @@ void attn_fwd_kernel(AttnArgs a) {
           p[v] = y * r;
         }
       } else {
+        float cb[16];
         #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int kl_idx = M::key_of(kb, v, hl);
-          const unsigned rel = (unsigned)(p_lane - (j0 + kl_idx));
-          float cb = sm.pos_t[min(rel, (unsigned)(n_pos - 1))];
-          if (has_time) {
-            int z;
-            if (small_span) {
-              const int32_t dt = tsq_lo - sm.ts_lo[buf][kl_idx];
+          const unsigned rel = (unsigned)(p_lane - (j0 + M::key_of(kb, v, hl)));
+          cb[v] = tab.pos_t[min(rel, (unsigned)(n_pos - 1))];
+        }
+        if (has_time) {
+          if (small_span) {
+            #pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int32_t dt = tsq_lo - st.ts_lo[M::key_of(kb, v, hl)];
               const uint32_t x = (uint32_t)(dt < 0 ? -dt : dt) + 1u;
-              z = __builtin_clz(x) + 32;
-            } else {
-              const int64_t dt = tsq - sm.ts64[buf][kl_idx];
-              const uint64_t x = (uint64_t)(dt < 0 ? -dt : dt) + 1u;
-              z = __builtin_clzll(x);
+              cb[v] += tab.time_t[__builtin_clz(x) + 32];
             }
-            cb += sm.time_t[z];
+          } else {
+            #pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int64_t dt = tsq - st.ts64[M::key_of(kb, v, hl)];
+              const uint64_t x = (uint64_t)(dt < 0 ? -dt : dt) + 1u;
+              cb[v] += tab.time_t[__builtin_clzll(x)];
+            }
           }
-          const float y = fmaf(acc[v], sc, cb);
+        }
+        #pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float y = fmaf(acc[v], sc, cb[v]);
           const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
           p[v] = y * r;
         }
@@ -370,13 +428,20 @@ void attn_fwd_kernel(AttnArgs a) {
           #pragma unroll
           for (int e = 0; e < 8; ++e) pb[c][e] = (bf16)p[8 * c + e];
         }
+        bf16x8 vop[G::NDB][2];
         #pragma unroll
         for (int db = 0; db < G::NDB; ++db) {
           #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            const bf16x8 vop = *(const bf16x8*)(vl + G::v_off(32 * db + l32, 2 * (2 * kb + c) + hl));
-            oacc[db] = M::run(vop, pb[c], oacc[db]);
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vl + v_tr_off(db, 2 * kb + c, 0)));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vl + v_tr_off(db, 2 * kb + c, 1)));
+            vop[db][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           }
+        }
+        #pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+          #pragma unroll
+          for (int c = 0; c < 2; ++c) oacc[db] = M::run(vop[db][c], pb[c], oacc[db]);
         }
       } else {
         #pragma unroll
@@ -384,30 +449,32 @@ void attn_fwd_kernel(AttnArgs a) {
           #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int key = M::key_of(kb, v, hl);
-            const float vop = *(const float*)(vl + G::v_off(32 * db + l32, key / 4) + (key % 4) * 4);
-            oacc[db] = M::run(vop, p[v], oacc[db]);
+            const int d = 32 * db + l32;
+            const float vv = *(const float*)(vl + G::v_off(key, d / 4) + (d % 4) * 4);
+            oacc[db] = M::run(vv, p[v], oacc[db]);
           }
         }
       }
     }
   };
 
-  // ---- main loop over key tiles (double-buffered LDS, one barrier per tile)
+  // ---- main loop over key tiles: compute one stage while the next streams in
   const int ntiles = k_end > k_begin ? (int)ceil_div(k_end - k_begin, KT) : 0;
   if (ntiles > 0) {
-    load_tile(k_begin);
-    store_tile(0, k_begin);
-    if (ntiles > 1) load_tile(k_begin + KT);
+    issue_tile(st0, k_begin);
+    finish_tile(st0);
+  } else {
+    __syncthreads();  // tables
   }
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = 0; t < ntiles; t += 2) {
     const int j0 = k_begin + t * KT;
-    compute_tile(t & 1, j0);
-    if (t + 1 < ntiles) {
-      store_tile((t + 1) & 1, j0 + KT);
-      if (t + 2 < ntiles) load_tile(j0 + 2 * KT);
-    }
-    __syncthreads();
+    if (t + 1 < ntiles) issue_tile(st1, j0 + KT);
+    compute_tile(st0, j0);
+    if (t + 1 >= ntiles) break;
+    finish_tile(st1);
+    if (t + 2 < ntiles) issue_tile(st0, j0 + 2 * KT);
+    compute_tile(st1, j0 + KT);
+    if (t + 2 < ntiles) finish_tile(st0);
   }
 
   // ---- M-FALCON: a candidate's own key (relative position 0, dt = 0) -------
@@ -426,7 +493,7 @@ void attn_fwd_kernel(AttnArgs a) {
       }
     }
     dot += __shfl_xor(dot, 32);
-    const float y = fmaf(dot, sc, sm.pos_t[0] + sm.time_t[63]);
+    const float y = fmaf(dot, sc, tab.pos_t[0] + tab.time_t[63]);
     const float pself = y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
     #pragma unroll
     for (int db = 0; db < G::NDB; ++db) {
@@ -439,9 +506,13 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: scale by -ln2 / N, stage through LDS, coalesced store -----
+  // Rows 0..63 are staged in stage 0's memory and rows 64..127 in stage 1's
+  // (each holds 64 rows of D fp32 values); chunks are XOR-swizzled by row.
+  __syncthreads();  // every wave is done reading the stages
   const float oscale = -LN2 / (float)n_norm;
-  float* st = (float*)&sm.kv[0][0][0];
   constexpr int OCPR = D / 4;  // 16-byte chunks per output row
+  static_assert(sizeof(Stage<T, D>) >= 64 * D * 4, "output staging fits one stage per 64 rows");
+  auto ostage = [&](int r) { return (float*)(r < 64 ? (unsigned char*)&st0 : (unsigned char*)&st1) + (r & 63) * D; };
   #pragma unroll
   for (int db = 0; db < G::NDB; ++db) {
     #pragma unroll
@@ -449,7 +520,7 @@ void attn_fwd_kernel(AttnArgs a) {
       const int c = (32 * db + 8 * g + 4 * hl) / 4;
       f32x4 x = {oacc[db][4 * g] * oscale, oacc[db][4 * g + 1] * oscale, oacc[db][4 * g + 2] * oscale,
                  oacc[db][4 * g + 3] * oscale};
-      *(f32x4*)(st + (row_w * OCPR + (c ^ (row_w % OCPR))) * 4) = x;
+      *(f32x4*)(ostage(row_w) + (c ^ (row_w % OCPR)) * 4) = x;
     }
   }
   __syncthreads();
@@ -457,7 +528,7 @@ void attn_fwd_kernel(AttnArgs a) {
   for (int i = tid; i < QT * OCPR; i += NTHREADS) {
     const int r = i / OCPR, c = i % OCPR;
     if (r < q_len && q_off + q_start + r < a.Tq && it.chunk < a.n_chunks) {
-      const f32x4 x = *(const f32x4*)(st + (r * OCPR + (c ^ (r % OCPR))) * 4);
+      const f32x4 x = *(const f32x4*)(ostage(r) + (c ^ (r % OCPR)) * 4);
       *(f32x4*)(obase + ((q_off + q_start + r) * H + h) * D + c * 4) = x;
     }
   }

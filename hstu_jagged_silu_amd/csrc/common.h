@@ -38,9 +38,12 @@ struct WorkItem {
 };
 
 // Workspace layout (bytes), shared by the scheduler, the attention kernel
-// and the epilogue: [header 256 B][items][per-user scratch][O partials].
+// and the epilogue: [header 256 B][items][per-user scratch][key timestamp
+// ranges][O partials].
 struct WsLayout {
-  size_t items_off, scratch_off, o_off, total;
+  size_t items_off, scratch_off, stats_off, o_off, total;
+  int64_t n_stat_blocks;  // key timestamp ranges (pairs of int64)
+  int32_t stat_stride;    // cached path: key tiles per user
   int64_t max_items;
   int32_t n_chunks;       // key splits (1 except on the cached path)
   int32_t chunk_keys;     // keys per split (multiple of KT)

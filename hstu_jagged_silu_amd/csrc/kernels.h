@@ -32,6 +32,11 @@ struct AttnArgs {
   float* o;                      // [n_chunks][Tq][H*D] fp32, scaled attention output
   int64_t o_chunk_stride;        // elements between key splits
   int32_t n_chunks;              // key splits the O buffer holds
+  // key timestamp range per 64-key block: jagged variants index packed rows
+  // (block i = rows [64i, 64i + 64)), the cached path indexes [b][key tile]
+  const int64_t* tstats;         // pairs (min, max)
+  int64_t n_stat_blocks;         // jagged: number of packed blocks
+  int32_t stat_stride;           // cached: key tiles per user
 };
 
 // Arguments of the single-workgroup jagged tile scheduler.
@@ -47,6 +52,14 @@ struct SchedArgs {
   int32_t* prefix;               // [B+1] scratch
   WorkItem* items;
   int32_t* count;
+  // key timestamp ranges, computed by the workgroups after the first
+  int64_t* tstats;
+  int64_t n_stat_blocks;         // blocks to fill
+  const int64_t* ts;             // jagged: key timestamps [Tk]
+  int64_t Tk;                    // jagged: key rows
+  const int64_t* ts_pages;       // cached
+  const int32_t* page_table;
+  int32_t num_pages, max_pages, stat_stride;
 };
 
 // Arguments of the LayerNorm + U gating epilogue (sums key splits first).
@@ -83,7 +96,7 @@ struct AppendArgs {
   int64_t T;
 };
 
-hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
+hipError_t launch_sched(const SchedArgs& a, hipStream_t s);  // scheduler + key timestamp ranges
 hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int mode, int64_t grid, hipStream_t s);
 hipError_t launch_ln_gate(const LnArgs& a, int dtype, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);

@@ -10,9 +10,10 @@
 // processing time). Masked key tiles are never listed (causal tile skipping):
 // an item's key range ends at its last row's limit.
 //
-// One workgroup of 1024 threads: count items per user, scan, histogram the
-// costs, scan the histogram from the top, scatter. Runs on the caller's
-// stream ahead of the attention kernel; no host synchronisation.
+// Workgroup 0 (1024 threads): count items per user, scan, histogram the
+// costs, scan the histogram from the top, scatter. The other workgroups of
+// the same launch compute key timestamp ranges. Runs on the caller's stream
+// ahead of the attention kernel; no host synchronisation.
 #include "kernels.h"
 
 namespace hstu {
@@ -112,7 +113,44 @@ __device__ inline int block_scan(int x, int* tmp, int& excl) {
   return total;
 }
 
+// Timestamp range (min, max) of every 64-key block, one wave per block. The
+// attention kernel uses it to decide per tile whether the time bucket is the
+// same for every pair. Jagged keys: block i covers packed rows [64i, 64i+64)
+// (it may straddle users; a wider range only makes the test conservative).
+// Cached keys: block (b, kt) covers the valid keys of that user's page kt.
+__device__ void key_time_ranges(const SchedArgs& a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)(blockIdx.x - 1) * (SCHED_THREADS / 64) + (threadIdx.x >> 6);
+  if (blk >= a.n_stat_blocks) return;
+  bool ok;
+  int64_t v = 0;
+  if (a.mode == MODE_CACHED) {
+    const int b = (int)(blk / a.stat_stride), kt = (int)(blk % a.stat_stride);
+    const int kcount = a.cache_lens[b] + (a.offsets[b + 1] - a.offsets[b]);
+    const int page = kt < a.max_pages ? a.page_table[(int64_t)b * a.max_pages + kt] : -1;
+    ok = kt * KT + lane < kcount && page >= 0 && page < a.num_pages;
+    if (ok) v = a.ts_pages[(int64_t)page * PAGE + lane];
+  } else {
+    const int64_t r = blk * KT + lane;
+    ok = r < a.Tk;
+    if (ok) v = a.ts[r];
+  }
+  int64_t mn = ok ? v : INT64_MAX, mx = ok ? v : INT64_MIN;
+  for (int m = 32; m >= 1; m >>= 1) {
+    mn = min(mn, (int64_t)__shfl_xor((long long)mn, m));
+    mx = max(mx, (int64_t)__shfl_xor((long long)mx, m));
+  }
+  if (lane == 0) {
+    a.tstats[2 * blk] = mn;
+    a.tstats[2 * blk + 1] = mx;
+  }
+}
+
 __global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(SchedArgs a) {
+  if (blockIdx.x > 0) {
+    key_time_ranges(a);
+    return;
+  }
   __shared__ int tmp[SCHED_THREADS];
   __shared__ int hist[NBINS];
   __shared__ int start[NBINS];
@@ -180,7 +218,8 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(SchedArgs a) {
 }
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(SCHED_THREADS), 0, s, a);
+  const int64_t grid = 1 + ceil_div(a.n_stat_blocks, SCHED_THREADS / 64);
+  hipLaunchKernelGGL(sched_kernel, dim3((unsigned)grid), dim3(SCHED_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

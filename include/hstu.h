@@ -120,6 +120,7 @@ typedef struct {
  *   k_pages, v_pages  [num_pages, H, page_size, d] in the layer dtype
  *   ts_pages          int64 [num_pages, page_size]
  *   page_table        int32 [batch, max_pages_per_seq]; -1 = no page
+ *   num_pages, max_pages_per_seq  >= 1
  *   page_size         must be 64
  * The caller owns the pages and the table and decides which pages a user
  * holds; the library never allocates, frees or evicts pages.
