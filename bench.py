@@ -241,6 +241,9 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=8192)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MiB; used to scale "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -294,6 +297,19 @@ def main():
         "epilogue": {"bound": "hbm", "achieved_gbs": round(ln_bytes / (ln_ms * 1e-3) / 1e9, 1),
                      "peak_gbs": PEAK_HBM_GBS, "bytes": ln_bytes},
     }
+    if args.copy_calibration_mib > 0:
+        # a plain device-to-device copy of n bytes; a 1 GiB write in between
+        # evicts the source from L2 and the 256 MB Infinity Cache first
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        flush.fill_(3)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
+        del src, dst, flush
     if not args.no_variants:
         variants = {}
         for name, fn in (("kv_cache_delta", bench_cached), ("mfalcon", bench_mfalcon),
