@@ -361,8 +361,12 @@ class HipEvent:
         return float(ms.value)
 
     def __del__(self):
-        if self.cuda_event and HipEvent._hip is not None:
-            HipEvent._hip.hipEventDestroy(self.cuda_event)
+        hip = getattr(HipEvent, "_hip", None)
+        if getattr(self, "cuda_event", None) and hip is not None:
+            try:
+                hip.hipEventDestroy(self.cuda_event)
+            except Exception:  # interpreter shutdown
+                pass
             self.cuda_event = None
 
 

@@ -42,6 +42,7 @@ template <typename T> struct Mfma;
 
 template <> struct Mfma<bf16> {
   static constexpr int KS = 16;  // reduction depth of one instruction
+  static constexpr int HLK = 8;  // key offset of the upper half-wave: key_of(kb, v, 1) - key_of(kb, v, 0)
   using op = bf16x8;
   __device__ static inline f32x16 run(op a, op b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -58,6 +59,7 @@ template <> struct Mfma<bf16> {
 
 template <> struct Mfma<float> {
   static constexpr int KS = 2;
+  static constexpr int HLK = 4;
   using op = float;
   __device__ static inline f32x16 run(op a, op b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -357,7 +359,31 @@ void attn_fwd_kernel(AttnArgs a) {
     const float cb_uniform = tab.pos_t[n_pos - 1] * (a.pos_tab ? 1.0f : 0.0f) + c_time;
     const bool small_span = span_hi < ((int64_t)1 << 31) - 2;
     const int32_t tsq_lo = (int32_t)tsq;
-    const int lim_rel = lim_lane - j0;
+    // per-lane bases: the per-register offsets key_of(kb, v, 0) are constants
+    const int lim_rel = lim_lane - j0 - M::HLK * hl;   // allowed iff key_of(kb, v, 0) <= lim_rel
+    const int rel_base = p_lane - j0 - M::HLK * hl;    // relative position = rel_base - key_of(kb, v, 0)
+    const int32_t* ts_lo_l = st.ts_lo + M::HLK * hl;
+    const int64_t* ts64_l = st.ts64 + M::HLK * hl;
+    const float c_pos = a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f;
+    // Two-bucket tiles (ordered timestamps whose |dt| range crosses one power
+    // of two) need only a threshold compare per element.
+    int two_thr = -1;   // |dt| >= two_thr selects the upper bucket
+    float c_lo = 0.0f, c_hi = 0.0f;
+    bool q_after_k = false;
+    if (!uniform && has_time && !time_uniform && small_span) {
+      int64_t lo = -1, hi = -1;
+      if (w_ts_min >= k_max) { lo = w_ts_min - k_max; hi = w_ts_max - k_min; q_after_k = true; }
+      else if (k_min >= w_ts_max) { lo = k_min - w_ts_max; hi = k_max - w_ts_min; }
+      if (lo >= 0) {
+        const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
+        const int blo = 63 - zlo, bhi = 63 - zhi;
+        if (bhi == blo + 1 && bhi <= n_time_eff - 1) {
+          two_thr = (1 << bhi) - 1;
+          c_lo = tab.time_t[zlo];
+          c_hi = tab.time_t[zhi];
+        }
+      }
+    }
 
     // one 32-key block at a time: S^T = K Q^T, SiLU, O^T += V^T P^T
     #pragma unroll
@@ -389,24 +415,35 @@ void attn_fwd_kernel(AttnArgs a) {
         float cb[16];
         #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const unsigned rel = (unsigned)(p_lane - (j0 + M::key_of(kb, v, hl)));
-          cb[v] = tab.pos_t[min(rel, (unsigned)(n_pos - 1))];
-        }
-        if (has_time) {
-          if (small_span) {
-            #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int32_t dt = tsq_lo - st.ts_lo[M::key_of(kb, v, hl)];
-              const uint32_t x = (uint32_t)(dt < 0 ? -dt : dt) + 1u;
-              cb[v] += tab.time_t[__builtin_clz(x) + 32];
-            }
+          if (pos_uniform) {
+            cb[v] = c_pos;
           } else {
-            #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int64_t dt = tsq - st.ts64[M::key_of(kb, v, hl)];
-              const uint64_t x = (uint64_t)(dt < 0 ? -dt : dt) + 1u;
-              cb[v] += tab.time_t[__builtin_clzll(x)];
-            }
+            const unsigned rel = (unsigned)(rel_base - M::key_of(kb, v, 0));
+            cb[v] = tab.pos_t[min(rel, (unsigned)(n_pos - 1))];
+          }
+        }
+        if (time_uniform) {
+          #pragma unroll
+          for (int v = 0; v < 16; ++v) cb[v] += c_time;
+        } else if (two_thr >= 0) {
+          #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int32_t dt = tsq_lo - ts_lo_l[M::key_of(kb, v, 0)];
+            cb[v] += ((q_after_k ? dt : -dt) >= two_thr) ? c_hi : c_lo;
+          }
+        } else if (small_span) {
+          #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int32_t dt = tsq_lo - ts_lo_l[M::key_of(kb, v, 0)];
+            const uint32_t x = (uint32_t)(dt < 0 ? -dt : dt) + 1u;
+            cb[v] += tab.time_t[__builtin_clz(x) + 32];
+          }
+        } else {
+          #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int64_t dt = tsq - ts64_l[M::key_of(kb, v, 0)];
+            const uint64_t x = (uint64_t)(dt < 0 ? -dt : dt) + 1u;
+            cb[v] += tab.time_t[__builtin_clzll(x)];
           }
         }
         #pragma unroll
@@ -418,7 +455,7 @@ void attn_fwd_kernel(AttnArgs a) {
       }
       if (need_mask) {
         #pragma unroll
-        for (int v = 0; v < 16; ++v) p[v] = (M::key_of(kb, v, hl) <= lim_rel) ? p[v] : 0.0f;
+        for (int v = 0; v < 16; ++v) p[v] = (M::key_of(kb, v, 0) <= lim_rel) ? p[v] : 0.0f;
       }
 
       if constexpr (sizeof(T) == 2) {
