@@ -11,7 +11,8 @@ Metric: algorithmic TFLOP/s = 4 * d * H * (allowed query-key pairs) / step
 time, and its fraction of the bf16 dense MFMA peak (2.5 PFLOP/s). The
 attention kernel's own time is measured with HIP events recorded around it on
 the launch stream (roofline.achieved). Other serving variants (KV-cache delta
-with paged append, M-FALCON, the jagged training shape) are reported under
+with paged append, M-FALCON, the jagged training shape, and the full layer with
+its f1/f2 products) are reported under
 "variants". The fp64 CPU oracle is timed on a bounded sample of the headline
 workload for reference (cpu_baseline).
 
@@ -205,6 +206,40 @@ def bench_training_shape(torch, hs, W, steps, warmup):
     }
 
 
+def bench_layer(torch, hs, W, steps, warmup):
+    """Full layer: f1 + SiLU (4 hipBLASLt products), attention, f2."""
+    inp = W.full_layer()
+    bf = torch.bfloat16
+    H, d, E = inp.num_heads, inp.head_dim, inp.x.shape[1]
+    x, w1, w2 = dev(torch, inp.x, bf), dev(torch, inp.w1, bf), dev(torch, inp.w2, bf)
+    ts, off = dev(torch, inp.ts), dev(torch, inp.seq_offsets)
+    p = hs.LayerParams(num_heads=H, head_dim=d, dtype=bf, pos_tab=dev(torch, inp.tables.pos),
+                       time_tab=dev(torch, inp.tables.time))
+    out = torch.empty_like(x)
+    ws = torch.empty(hs.hstu_layer_workspace_size(p, E, len(inp.lengths), inp.total, inp.max_len), dtype=torch.uint8,
+                     device="cuda")
+    fn = lambda ev: hs.hstu_layer_fwd(x, w1, w2, ts, off, inp.max_len, p, out=out, workspace=ws, timing_events=ev)
+    ms, evs = timed(fn, steps, warmup, torch)
+    T, HD = inp.total, H * d
+    f1_flop, f2_flop = 2 * T * E * 4 * HD, 2 * T * HD * E
+    attn_flop = 4 * d * H * hs.pair_count("full", [int(x) for x in inp.lengths])
+    f1_ms, attn_ms, f2_ms = mean_span(evs, 0, 1), mean_span(evs, 1, 2), mean_span(evs, 2, 3)
+    return {
+        "workload": inp.name,
+        "total_tokens": T,
+        "ms_per_step": round(ms, 4),
+        "tflops": round((f1_flop + f2_flop + attn_flop) / (ms * 1e-3) / 1e12, 2),
+        "f1_silu_ms": round(f1_ms, 4),
+        "f1_tflops": round(f1_flop / (f1_ms * 1e-3) / 1e12, 2),
+        "attention_ms": round(attn_ms, 4),
+        "attention_tflops": round(attn_flop / (attn_ms * 1e-3) / 1e12, 2),
+        "f2_ms": round(f2_ms, 4),
+        "f2_tflops": round(f2_flop / (f2_ms * 1e-3) / 1e12, 2),
+        "algorithmic_gflop": {"f1": round(f1_flop / 1e9, 1), "attention": round(attn_flop / 1e9, 1),
+                              "f2": round(f2_flop / 1e9, 1)},
+    }
+
+
 def cpu_baseline(inp, rows):
     """The fp64 oracle on rows 0..rows-1 of user 0 (all heads, N = 8,192): exactly
     those rows of the headline workload. Returns the cpu_baseline object."""
@@ -313,7 +348,7 @@ def main():
     if not args.no_variants:
         variants = {}
         for name, fn in (("kv_cache_delta", bench_cached), ("mfalcon", bench_mfalcon),
-                         ("jagged_training_shape", bench_training_shape)):
+                         ("jagged_training_shape", bench_training_shape), ("full_layer", bench_layer)):
             log(f"variant {name}")
             variants[name] = fn(torch, hs, W, args.steps, args.warmup)
             log(f"  {variants[name]}")

@@ -32,7 +32,8 @@ PAGE_SIZE = 64
 
 EXPORTED_SYMBOLS = (
     "hstu_status_string", "hstu_version", "hstu_workspace_size", "hstu_attn_fwd",
-    "hstu_kv_append", "hstu_attn_fwd_cached", "hstu_mfalcon_fwd",
+    "hstu_kv_append", "hstu_attn_fwd_cached", "hstu_mfalcon_fwd", "hstu_layer_workspace_size",
+    "hstu_layer_fwd",
 )
 
 
@@ -59,6 +60,10 @@ class _KVCache(ctypes.Structure):
     ]
 
 
+class _LayerWeights(ctypes.Structure):
+    _fields_ = [("embed_dim", ctypes.c_int32), ("w1", ctypes.c_void_p), ("w2", ctypes.c_void_p)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
@@ -81,6 +86,11 @@ def _load():
     lib.hstu_attn_fwd_cached.argtypes = [P, i32, vp, vp, i32, i32, i64, vp, vp, vp, K, vp, vp, sz, vp]
     lib.hstu_mfalcon_fwd.restype = ctypes.c_int
     lib.hstu_mfalcon_fwd.argtypes = [P, i32, vp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    W = ctypes.POINTER(_LayerWeights)
+    lib.hstu_layer_workspace_size.restype = sz
+    lib.hstu_layer_workspace_size.argtypes = [P, i32, i32, i64, i32]
+    lib.hstu_layer_fwd.restype = ctypes.c_int
+    lib.hstu_layer_fwd.argtypes = [P, W, i32, vp, i32, i64, vp, vp, vp, vp, sz, vp]
     return lib
 
 
@@ -248,6 +258,47 @@ def hstu_mfalcon_fwd(q, k, v, u, ts, seq_offsets, num_candidates, max_len: int, 
                                  q.data_ptr(), k.data_ptr(), v.data_ptr(), u.data_ptr(), ts.data_ptr(),
                                  y.data_ptr(), ws.data_ptr(), ws.numel(), _stream()), "hstu_mfalcon_fwd")
     return y
+
+
+def hstu_layer_workspace_size(params: LayerParams, embed_dim: int, batch: int, total_tokens: int,
+                              max_len: int) -> int:
+    """Workspace bytes of one hstu_layer_fwd call."""
+    p = params.c_struct()
+    n = int(_lib.hstu_layer_workspace_size(ctypes.byref(p), embed_dim, batch, total_tokens, max_len))
+    if n == 0:
+        raise HstuError("hstu_layer_workspace_size: invalid arguments")
+    return n
+
+
+def hstu_layer_fwd(x, w1, w2, ts, seq_offsets, max_len: int, params: LayerParams, *, out=None,
+                   workspace=None, timing_events=None):
+    """Full layer: [U|V|Q|K] = SiLU(x w1), attention, out = A w2.
+
+    x [T, E], w1 [E, 4*H*d], w2 [H*d, E], all bf16 on the GPU; ts int64 [T];
+    seq_offsets int32 [B+1]. Returns out [T, E]."""
+    H, d = params.num_heads, params.head_dim
+    for name, t in (("x", x), ("w1", w1), ("w2", w2)):
+        _device_tensor(t, params.dtype, name)
+        if t.dim() != 2:
+            raise ValueError(f"{name} must be 2-D")
+    T, E = x.shape
+    if w1.shape != (E, 4 * H * d) or w2.shape != (H * d, E):
+        raise ValueError(f"w1 must be [{E}, {4 * H * d}] and w2 [{H * d}, {E}]")
+    _device_tensor(ts, torch.int64, "ts")
+    _device_tensor(seq_offsets, torch.int32, "seq_offsets")
+    if ts.shape != (T,):
+        raise ValueError("ts must be [T]")
+    B = seq_offsets.shape[0] - 1
+    out = torch.empty_like(x) if out is None else out
+    _device_tensor(out, params.dtype, "out")
+    nbytes = hstu_layer_workspace_size(params, E, B, T, max_len)
+    ws = _workspace(workspace, nbytes, x.device)
+    p = params.c_struct(timing_events)
+    wts = _LayerWeights(E, w1.data_ptr(), w2.data_ptr())
+    _check(_lib.hstu_layer_fwd(ctypes.byref(p), ctypes.byref(wts), B, seq_offsets.data_ptr(), max_len, T,
+                               x.data_ptr(), ts.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
+           "hstu_layer_fwd")
+    return out
 
 
 @dataclasses.dataclass

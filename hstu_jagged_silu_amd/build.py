@@ -1,7 +1,7 @@
 """Build the HIP library libhstu.so in place for gfx950 with hipcc.
 
-Sources: csrc/*.hip (kernels) and csrc/api.cpp (the C ABI declared in
-include/hstu.h). Objects go to _build/ next to this file; the shared library
+Sources: csrc/*.hip (kernels), csrc/api.cpp and csrc/layer.cpp (the C ABI
+declared in include/hstu.h; the layer links hipBLASLt). Objects go to _build/ next to this file; the shared library
 lands beside the package's __init__.py, where the binding loads it.
 """
 from __future__ import annotations
@@ -65,7 +65,10 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc()))), "lib")
+    cmd = ([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs +
+           # the full layer's two dense products run on hipBLASLt
+           ["-L", rocm_lib, f"-Wl,-rpath,{rocm_lib}", "-lhipblaslt"])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

@@ -219,6 +219,47 @@ hstu_status_t hstu_mfalcon_fwd(const hstu_params_t* params, int32_t batch, const
                                const int64_t* ts, void* y, void* ws, size_t ws_bytes,
                                hipStream_t stream);
 
+/*
+ * Full HSTU layer ("How Generative Recommenders Are Redefining RecSys at
+ * Scale", Takeaways: elementwise gating before the output projection;
+ * "Generative recommenders at scale", section "Inside NVIDIA's GPU-native
+ * stack for HSTU and Semantic IDs"). With E = embed_dim and HD = H*d:
+ *
+ *   [U | V | Q | K] = SiLU(X W1)        X [T, E], W1 [E, 4*HD], split in
+ *                                       this column order, each [T, HD]
+ *   A = hstu_attn_fwd(Q, K, V, U, ts)   the full causal path above
+ *   out = A W2                          W2 [HD, E], out [T, E]
+ *
+ * f1 and f2 have no bias term. The two products run on hipBLASLt (f1 with
+ * its SiLU epilogue, one product per U/V/Q/K column block, each writing a
+ * packed [T, HD] buffer in the workspace); the attention runs on this
+ * library's kernels. Only HSTU_BF16 is supported (HSTU_ERR_UNSUPPORTED for
+ * HSTU_F32): bf16 operands, fp32 accumulation, bf16 U, V, Q, K, A and out.
+ *   weights->w1, weights->w2  row-major device matrices in bf16
+ *   x    [T, E] bf16; ts int64 [T]; out [T, E] bf16 (must not alias x)
+ *   ws   at least hstu_layer_workspace_size(...) bytes
+ * params->timing_events, if set, are recorded [0] before f1, [1] before the
+ * attention, [2] before f2, [3] after f2. The first call on a device
+ * creates a hipBLASLt handle for it, kept until the process ends (the only
+ * host state the library holds); later calls reuse it and the chosen GEMM
+ * algorithms. Callable from several host threads.
+ */
+typedef struct {
+  int32_t embed_dim;  /* E >= 1, multiple of 8 */
+  const void* w1;     /* [E, 4 * H * d] */
+  const void* w2;     /* [H * d, E] */
+} hstu_layer_weights_t;
+
+/* Workspace bytes of hstu_layer_fwd; 0 for invalid arguments. Monotone in
+ * every argument like hstu_workspace_size. */
+size_t hstu_layer_workspace_size(const hstu_params_t* params, int32_t embed_dim, int32_t batch,
+                                 int64_t total_tokens, int32_t max_len);
+
+hstu_status_t hstu_layer_fwd(const hstu_params_t* params, const hstu_layer_weights_t* weights,
+                             int32_t batch, const int32_t* seq_offsets, int32_t max_len,
+                             int64_t total_tokens, const void* x, const int64_t* ts, void* out,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

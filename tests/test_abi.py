@@ -56,6 +56,8 @@ int main(void) {
   P(hstu_kv_cache_t, k_pages); P(hstu_kv_cache_t, v_pages); P(hstu_kv_cache_t, ts_pages);
   P(hstu_kv_cache_t, page_table); P(hstu_kv_cache_t, num_pages); P(hstu_kv_cache_t, page_size);
   P(hstu_kv_cache_t, max_pages_per_seq);
+  printf("hstu_layer_weights_t %zu\n", sizeof(hstu_layer_weights_t));
+  P(hstu_layer_weights_t, embed_dim); P(hstu_layer_weights_t, w1); P(hstu_layer_weights_t, w2);
   return 0;
 }
 ''')
@@ -71,6 +73,9 @@ int main(void) {
         assert int(got[f"hstu_params_t.{name}"]) == getattr(hs._Params, name).offset, name
     for name, _ in hs._KVCache._fields_:
         assert int(got[f"hstu_kv_cache_t.{name}"]) == getattr(hs._KVCache, name).offset, name
+    assert int(got["hstu_layer_weights_t"]) == ctypes.sizeof(hs._LayerWeights)
+    for name, _ in hs._LayerWeights._fields_:
+        assert int(got[f"hstu_layer_weights_t.{name}"]) == getattr(hs._LayerWeights, name).offset, name
 
 
 def test_version_and_status_strings():
@@ -169,6 +174,33 @@ def test_cached_and_mfalcon_and_append_reject_bad_arguments():
     assert r == INVALID
     r = lib.hstu_mfalcon_fwd(ctypes.byref(p), 2, FAKE, FAKE, 16, 32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, None)
     assert r == WORKSPACE
+
+
+def test_layer_workspace_and_bad_arguments_before_launch():
+    lib = hs.lib()
+    p = _params(num_heads=8)
+    size = lambda p, E, B, T, L: int(lib.hstu_layer_workspace_size(ctypes.byref(p), E, B, T, L))
+    n = size(p, 1024, 16, 45800, 8192)
+    # U, V, Q, K and the attention output in bf16, plus the attention workspace
+    assert n >= 5 * 45800 * 1024 * 2 + _ws(0, p, 16, 45800, 8192)
+    assert size(p, 1024, 16, 45801, 8192) >= n and size(p, 1024, 17, 45800, 8192) >= n
+    assert size(p, 1024, 16, 45800, 8193) >= n
+    assert size(p, 1020, 16, 45800, 8192) == 0          # E not a multiple of 8
+    assert size(_params(num_heads=8, dtype=0), 1024, 16, 45800, 8192) == 0  # fp32 layer unsupported
+    f = lib.hstu_layer_fwd
+    w = hs._LayerWeights(1024, FAKE, FAKE)
+
+    def call(p, w=w, B=2, T=32, x=FAKE, wsb=0):
+        return f(ctypes.byref(p), ctypes.byref(w), B, FAKE, 16, T, x, FAKE, FAKE, FAKE, wsb, None)
+
+    assert call(_params(dtype=0)) == UNSUPPORTED
+    assert call(p, w=hs._LayerWeights(1020, FAKE, FAKE)) == INVALID
+    assert call(p, w=hs._LayerWeights(1024, None, FAKE)) == INVALID
+    assert call(p, x=None) == INVALID
+    assert call(p, x=FAKE + 2) == INVALID
+    assert call(_params(head_dim=48)) == INVALID
+    assert call(p) == WORKSPACE
+    assert call(p, B=0) == OK
 
 
 def test_pair_count_matches_closed_forms():
