@@ -30,12 +30,21 @@
 //     with b' = -log2(e) (P[.] + T[.]); then SiLU(x) = -ln2 * y / (1 + 2^y),
 //     and the -ln2 / N factor moves to the epilogue. Far from the diagonal a
 //     wave tile's bias is usually one constant (position clamped, one time
-//     bucket); the per-element bucket path only runs where it varies.
+//     bucket); the per-element bucket path only runs where it varies, and
+//     there a masked pair gets a huge bias that makes its SiLU exactly 0.
+//   * Per tile, the score MFMAs of both 32-key blocks, the P V MFMAs and the
+//     accumulators are shared by every tile kind; only the SiLU inputs
+//     differ. The compiler then keeps one register assignment for O and
+//     overlaps the second block's SiLU with the P V MFMAs.
 #include "kernels.h"
 
 namespace hstu {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Bias value of a masked pair. With y = s * (-alpha log2 e) + MASKED_Y finite
+// and 2^y = +inf, the SiLU form y / (1 + 2^y) is exactly 0 (rcp(inf) = 0).
+constexpr float MASKED_Y = 1.0e30f;
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 template <typename T> struct Mfma;
@@ -329,10 +338,25 @@ void attn_fwd_kernel(AttnArgs a) {
     return G::v_off(key, d / G::EPC) + (d % G::EPC) * (int)sizeof(T);
   };
 
+  // Per-lane byte offsets of this lane's MFMA operand reads inside a stage's K
+  // and V tiles, for key block 0 (the second 32-key block adds 32 rows, the
+  // second 16-key half of a V operand 16 rows: compile-time offsets).
+  uint32_t koff[G::NQOP], voff[G::NDB][2];
+  {
+    const int kr = M::krow(0, l32);
+    #pragma unroll
+    for (int s = 0; s < G::NQOP; ++s) koff[s] = (uint32_t)G::k_off(kr, sizeof(T) == 2 ? 2 * s + hl : 0);
+    #pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+      voff[db][0] = (uint32_t)v_tr_off(db, 0, 0);
+      voff[db][1] = (uint32_t)v_tr_off(db, 0, 1);
+    }
+  }
+
+  using LB = __attribute__((address_space(3))) unsigned char;
+
   auto compute_tile = [&](Stage<T, D>& st, int j0) {
     if (!w_rows || j0 > w_lim_max) return;  // every pair of this wave masked
-    const unsigned char* kl = st.k;
-    const unsigned char* vl = st.v;
 
     // classify the wave tile: mask, constant bias, or per-element bias
     const bool need_mask = j0 + KT - 1 > w_lim_min;
@@ -356,7 +380,7 @@ void attn_fwd_kernel(AttnArgs a) {
       }
     }
     const bool uniform = pos_uniform && time_uniform;
-    const float cb_uniform = tab.pos_t[n_pos - 1] * (a.pos_tab ? 1.0f : 0.0f) + c_time;
+    const float c_pos = a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f;
     const bool small_span = span_hi < ((int64_t)1 << 31) - 2;
     const int32_t tsq_lo = (int32_t)tsq;
     // per-lane bases: the per-register offsets key_of(kb, v, 0) are constants
@@ -364,123 +388,154 @@ void attn_fwd_kernel(AttnArgs a) {
     const int rel_base = p_lane - j0 - M::HLK * hl;    // relative position = rel_base - key_of(kb, v, 0)
     const int32_t* ts_lo_l = st.ts_lo + M::HLK * hl;
     const int64_t* ts64_l = st.ts64 + M::HLK * hl;
-    const float c_pos = a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f;
-    // Two-bucket tiles (ordered timestamps whose |dt| range crosses one power
-    // of two) need only a threshold compare per element.
-    int two_thr = -1;   // |dt| >= two_thr selects the upper bucket
-    float c_lo = 0.0f, c_hi = 0.0f;
-    bool q_after_k = false;
-    if (!uniform && has_time && !time_uniform && small_span) {
-      int64_t lo = -1, hi = -1;
-      if (w_ts_min >= k_max) { lo = w_ts_min - k_max; hi = w_ts_max - k_min; q_after_k = true; }
-      else if (k_min >= w_ts_max) { lo = k_min - w_ts_max; hi = k_max - w_ts_min; }
-      if (lo >= 0) {
-        const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
-        const int blo = 63 - zlo, bhi = 63 - zhi;
-        if (bhi == blo + 1 && bhi <= n_time_eff - 1) {
-          two_thr = (1 << bhi) - 1;
-          c_lo = tab.time_t[zlo];
-          c_hi = tab.time_t[zhi];
+
+    // Per-element bias of key block kb, scaled by -log2(e); masked pairs get
+    // MASKED_Y when fold_mask (SiLU of it is exactly zero).
+    auto element_bias = [&](int kb, float* cb, bool fold_mask) {
+      // Two-bucket tiles (ordered timestamps whose |dt| range crosses one
+      // power of two) need only a threshold compare per element.
+      int two_thr = -1;   // |dt| >= two_thr selects the upper bucket
+      float c_lo = 0.0f, c_hi = 0.0f;
+      bool q_after_k = false;
+      if (has_time && !time_uniform && small_span) {
+        int64_t lo = -1, hi = -1;
+        if (w_ts_min >= k_max) { lo = w_ts_min - k_max; hi = w_ts_max - k_min; q_after_k = true; }
+        else if (k_min >= w_ts_max) { lo = k_min - w_ts_max; hi = k_max - w_ts_min; }
+        if (lo >= 0) {
+          const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
+          const int blo = 63 - zlo, bhi = 63 - zhi;
+          if (bhi == blo + 1 && bhi <= n_time_eff - 1) {
+            two_thr = (1 << bhi) - 1;
+            c_lo = tab.time_t[zlo];
+            c_hi = tab.time_t[zhi];
+          }
         }
       }
-    }
-
-    // one 32-key block at a time: S^T = K Q^T, SiLU, O^T += V^T P^T
-    #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      typename M::op kop[G::NQOP];
-      const int kr = M::krow(kb, l32);
       #pragma unroll
-      for (int s = 0; s < G::NQOP; ++s) {
-        if constexpr (sizeof(T) == 2) {
-          kop[s] = *(const bf16x8*)(kl + G::k_off(kr, 2 * s + hl));
+      for (int v = 0; v < 16; ++v) {
+        if (pos_uniform) {
+          cb[v] = c_pos;
         } else {
-          const int d = 2 * s + hl;
-          kop[s] = *(const float*)(kl + G::k_off(kr, d / 4) + (d % 4) * 4);
+          const unsigned rel = (unsigned)(rel_base - M::key_of(kb, v, 0));
+          cb[v] = tab.pos_t[min(rel, (unsigned)(n_pos - 1))];
         }
       }
-      f32x16 acc = f32x16{};
-      #pragma unroll
-      for (int s = 0; s < G::NQOP; ++s) acc = M::run(kop[s], qop[s], acc);
-
-      float p[16];
-      if (uniform) {
+      if (time_uniform) {
+        #pragma unroll
+        for (int v = 0; v < 16; ++v) cb[v] += c_time;
+      } else if (two_thr >= 0) {
         #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float y = fmaf(acc[v], sc, cb_uniform);
-          const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
-          p[v] = y * r;
+          const int32_t dt = tsq_lo - ts_lo_l[M::key_of(kb, v, 0)];
+          cb[v] += ((q_after_k ? dt : -dt) >= two_thr) ? c_hi : c_lo;
+        }
+      } else if (small_span) {
+        #pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int32_t dt = tsq_lo - ts_lo_l[M::key_of(kb, v, 0)];
+          const uint32_t x = (uint32_t)(dt < 0 ? -dt : dt) + 1u;
+          cb[v] += tab.time_t[__builtin_clz(x) + 32];
         }
       } else {
-        float cb[16];
         #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          if (pos_uniform) {
-            cb[v] = c_pos;
-          } else {
-            const unsigned rel = (unsigned)(rel_base - M::key_of(kb, v, 0));
-            cb[v] = tab.pos_t[min(rel, (unsigned)(n_pos - 1))];
+          const int64_t dt = tsq - ts64_l[M::key_of(kb, v, 0)];
+          const uint64_t x = (uint64_t)(dt < 0 ? -dt : dt) + 1u;
+          cb[v] += tab.time_t[__builtin_clzll(x)];
+        }
+      }
+      if (fold_mask && need_mask) {
+        #pragma unroll
+        for (int v = 0; v < 16; ++v) cb[v] = (M::key_of(kb, v, 0) <= lim_rel) ? cb[v] : MASKED_Y;
+      }
+    };
+
+    if constexpr (sizeof(T) == 2) {
+      LB* kl = LDS_PTR(unsigned char, st.k);
+      LB* vl = LDS_PTR(unsigned char, st.v);
+      // S^T = K Q^T for the 32 keys of block kb
+      auto s_chain = [&](int kb) {
+        f32x16 acc = f32x16{};
+        #pragma unroll
+        for (int s = 0; s < G::NQOP; ++s) {
+          const bf16x8 kop = *(__attribute__((address_space(3))) const bf16x8*)(kl + koff[s] + kb * 32 * G::ROWB);
+          acc = M::run(kop, qop[s], acc);
+        }
+        return acc;
+      };
+      // O^T += V^T P^T for block kb; V^T operands from two transposing reads
+      auto pv = [&](int kb, const bf16x8* pb) {
+        #pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+          #pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const int o = (2 * kb + cc) * 16 * G::ROWB;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(vl + voff[db][0] + o));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(vl + voff[db][1] + o));
+            const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[db] = M::run(vop, pb[cc], oacc[db]);
           }
         }
-        if (time_uniform) {
-          #pragma unroll
-          for (int v = 0; v < 16; ++v) cb[v] += c_time;
-        } else if (two_thr >= 0) {
-          #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int32_t dt = tsq_lo - ts_lo_l[M::key_of(kb, v, 0)];
-            cb[v] += ((q_after_k ? dt : -dt) >= two_thr) ? c_hi : c_lo;
-          }
-        } else if (small_span) {
-          #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int32_t dt = tsq_lo - ts_lo_l[M::key_of(kb, v, 0)];
-            const uint32_t x = (uint32_t)(dt < 0 ? -dt : dt) + 1u;
-            cb[v] += tab.time_t[__builtin_clz(x) + 32];
-          }
-        } else {
-          #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int64_t dt = tsq - ts64_l[M::key_of(kb, v, 0)];
-            const uint64_t x = (uint64_t)(dt < 0 ? -dt : dt) + 1u;
-            cb[v] += tab.time_t[__builtin_clzll(x)];
-          }
-        }
+      };
+      // SiLU with y = s * (-alpha log2 e) + bias, packed to bf16
+      auto silu_pack = [&](const f32x16& acc, const float* cb, bf16x8* pb) {
         #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float y = fmaf(acc[v], sc, cb[v]);
-          const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
-          p[v] = y * r;
+          const float p = y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
+          pb[v >> 3][v & 7] = (bf16)p;
         }
-      }
-      if (need_mask) {
-        #pragma unroll
-        for (int v = 0; v < 16; ++v) p[v] = (M::key_of(kb, v, 0) <= lim_rel) ? p[v] : 0.0f;
-      }
+      };
 
-      if constexpr (sizeof(T) == 2) {
-        bf16x8 pb[2];
+      // Score MFMAs of both 32-key blocks, then SiLU (one bias constant, or
+      // per-element bias with the mask folded in), then the P V MFMAs. The
+      // accumulators are only touched by code shared by every tile.
+      const f32x16 s0 = s_chain(0);
+      const f32x16 s1 = s_chain(1);
+      bf16x8 p0[2], p1[2];
+      if (uniform && !need_mask) {
+        float cu[16];
         #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int v = 0; v < 16; ++v) cu[v] = c_pos + c_time;
+        silu_pack(s0, cu, p0);
+        silu_pack(s1, cu, p1);
+      } else {
+        float cb[16];
+        element_bias(0, cb, true);
+        silu_pack(s0, cb, p0);
+        element_bias(1, cb, true);
+        silu_pack(s1, cb, p1);
+      }
+      pv(0, p0);
+      pv(1, p1);
+    } else {
+      const unsigned char* kl = st.k;
+      const unsigned char* vl = st.v;
+      #pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float acc_p[16];
+        {
+          f32x16 acc = f32x16{};
+          const int kr = M::krow(kb, l32);
           #pragma unroll
-          for (int e = 0; e < 8; ++e) pb[c][e] = (bf16)p[8 * c + e];
-        }
-        bf16x8 vop[G::NDB][2];
-        #pragma unroll
-        for (int db = 0; db < G::NDB; ++db) {
+          for (int s = 0; s < G::NQOP; ++s) {
+            const int d = 2 * s + hl;
+            acc = M::run(*(const float*)(kl + G::k_off(kr, d / 4) + (d % 4) * 4), qop[s], acc);
+          }
+          float cb[16];
+          if (uniform) {
+            #pragma unroll
+            for (int v = 0; v < 16; ++v) cb[v] = c_pos + c_time;
+          } else {
+            element_bias(kb, cb, false);
+          }
           #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vl + v_tr_off(db, 2 * kb + c, 0)));
-            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vl + v_tr_off(db, 2 * kb + c, 1)));
-            vop[db][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          for (int v = 0; v < 16; ++v) {
+            const float y = fmaf(acc[v], sc, cb[v]);
+            acc_p[v] = y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
+            if (need_mask) acc_p[v] = (M::key_of(kb, v, 0) <= lim_rel) ? acc_p[v] : 0.0f;
           }
         }
-        #pragma unroll
-        for (int db = 0; db < G::NDB; ++db) {
-          #pragma unroll
-          for (int c = 0; c < 2; ++c) oacc[db] = M::run(vop[db][c], pb[c], oacc[db]);
-        }
-      } else {
         #pragma unroll
         for (int db = 0; db < G::NDB; ++db) {
           #pragma unroll
@@ -488,7 +543,7 @@ void attn_fwd_kernel(AttnArgs a) {
             const int key = M::key_of(kb, v, hl);
             const int d = 32 * db + l32;
             const float vv = *(const float*)(vl + G::v_off(key, d / 4) + (d % 4) * 4);
-            oacc[db] = M::run(vv, p[v], oacc[db]);
+            oacc[db] = M::run(vv, acc_p[v], oacc[db]);
           }
         }
       }
