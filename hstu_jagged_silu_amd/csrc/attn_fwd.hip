@@ -87,11 +87,18 @@ template <typename T, int D> struct Geo {
   static constexpr int NDB = D / 32;                    // 32-wide d blocks of O
   static constexpr int NQOP = D / Mfma<T>::KS;          // Q (and K) operands per lane per key block
   static_assert(NDMA >= 1 && NDMA * NWAVES * 1024 == TILE, "tile staging map");
-  // XOR swizzles on 16-byte chunks. K: MFMA operand reads (8 lanes, 8 rows,
-  // one chunk) hit distinct chunks. V (bf16): the transposing reads (16
-  // lanes: 4 consecutive rows x 2 adjacent chunks) hit 8 distinct chunks.
+  // XOR swizzles on 16-byte chunks, chosen so that every 256-byte LDS access
+  // window of an operand read touches 64 distinct banks. K: 16 lanes read 16
+  // different rows at one chunk. V (bf16): 32 lanes of a transposing read
+  // cover 4 consecutive rows x 64 bytes (d = 128: chunks 4db..4db+3, so the
+  // row index mod 4 must move the chunk group; d = 64: two rows share a
+  // window, rows r and r + 2 must differ; d = 32: one row per quarter).
   __device__ static inline int swz_k(int r) { return r % CPR; }
-  __device__ static inline int swz_v(int r) { return sizeof(T) == 2 ? (2 * r) % CPR : r % CPR; }
+  __device__ static inline int swz_v(int r) {
+    if constexpr (sizeof(T) == 4) return r % CPR;
+    else if constexpr (D == 128) return 4 * (r & 3);
+    else return (2 * r) % CPR;
+  }
   __device__ static inline int k_off(int r, int c) { return r * ROWB + ((c ^ swz_k(r)) << 4); }
   __device__ static inline int v_off(int r, int c) { return r * ROWB + ((c ^ swz_v(r)) << 4); }
 };
