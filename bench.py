@@ -101,7 +101,22 @@ def bench_full(torch, hs, W, steps, warmup):
     ms, evs = timed(fn, steps, warmup, torch)
     pairs = 4 * hs.pair_count("full", [int(x) for x in inp.lengths])
     flop = 4 * 128 * pairs
-    return inp, ms, evs, flop
+    return inp, ms, evs, flop, fn
+
+
+def cold_runs(torch, hs, fn, n=10, flush_mib=512):
+    """Attention-kernel time with L2 and the Infinity Cache flushed before each
+    call (a flush_mib write in between); returns per-call ms."""
+    flush = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda")
+    out = []
+    for i in range(n):
+        flush.fill_(i & 0xFF)
+        ev = [hs.HipEvent() for _ in range(4)]
+        fn(ev)
+        torch.cuda.synchronize()
+        out.append(ev[1].elapsed_ms(ev[2]))
+    del flush
+    return out
 
 
 def bench_cached(torch, hs, W, steps, warmup):
@@ -295,8 +310,11 @@ def main():
         sys.exit(1)
 
     log("headline: 8 x 8192, 4 x 128, bf16")
-    inp, ms, evs, flop = bench_full(torch, hs, W, args.steps, args.warmup)
+    inp, ms, evs, flop, step_fn = bench_full(torch, hs, W, args.steps, args.warmup)
     attn_ms = mean_span(evs, 1, 2)
+    attn_each = sorted(e[1].elapsed_ms(e[2]) for e in evs)
+    attn_median = attn_each[len(attn_each) // 2]
+    cold = sorted(cold_runs(torch, hs, step_fn))
     sched_ms = mean_span(evs, 0, 1)
     ln_ms = mean_span(evs, 2, 3)
     value = flop / (ms * 1e-3) / 1e12
@@ -326,7 +344,9 @@ def main():
                    "algorithmic_gflop": round(flop / 1e9, 3)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                     "kernel": "attn_fwd_kernel<bf16,128,full>", "kernel_ms": round(attn_ms, 4)},
+                     "kernel": "attn_fwd_kernel<bf16,128,full>", "kernel_ms": round(attn_ms, 4),
+                     "kernel_ms_median": round(attn_median, 4),
+                     "kernel_ms_cold_median": round(cold[len(cold) // 2], 4)},
         "kernels_ms": {"scheduler": round(sched_ms, 4), "attention": round(attn_ms, 4),
                        "ln_gate": round(ln_ms, 4)},
         "epilogue": {"bound": "hbm", "achieved_gbs": round(ln_bytes / (ln_ms * 1e-3) / 1e9, 1),
