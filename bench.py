@@ -196,6 +196,48 @@ def bench_mfalcon(torch, hs, W, steps, warmup):
     }
 
 
+def bench_mfalcon_paged(torch, hs, W, steps, warmup):
+    """M-FALCON with the history in the paged cache: only candidate rows are computed."""
+    import numpy as np
+    ci = W.mfalcon_scoring()
+    inp = ci.inputs
+    bf = torch.bfloat16
+    hist, cand = ci.split()
+    num_pages, table = ci.history_pages(8)
+    p = hs.LayerParams(num_heads=4, head_dim=128, dtype=bf, pos_tab=dev(torch, inp.tables.pos),
+                       time_tab=dev(torch, inp.tables.time))
+    cache = hs.PagedKVCache.empty(num_pages, 4, 128, dev(torch, table), dtype=bf)
+    hs.hstu_kv_append(cache, dev(torch, W.offsets_from_lengths(ci.hist_lens)),
+                      dev(torch, np.zeros(len(ci.hist_lens), np.int32)), dev(torch, inp.k[hist], bf),
+                      dev(torch, inp.v[hist], bf), dev(torch, inp.ts[hist]), p)
+    q, k, v, u = (dev(torch, x[cand], bf) for x in (inp.q, inp.k, inp.v, inp.u))
+    ts, coff, hl = dev(torch, inp.ts[cand]), dev(torch, W.offsets_from_lengths(ci.num_candidates)), \
+        dev(torch, ci.hist_lens)
+    max_cand, max_hist = int(ci.num_candidates.max()), int(ci.hist_lens.max())
+    y = torch.empty_like(u)
+    ws = torch.empty(hs.hstu_workspace_size(hs.HSTU_FN_MFALCON_CACHED, p, len(ci.hist_lens), len(cand), max_hist),
+                     dtype=torch.uint8, device="cuda")
+    fn = lambda ev: hs.hstu_mfalcon_fwd_cached(q, k, v, u, ts, coff, hl, max_cand, max_hist, cache, p, y=y,
+                                               workspace=ws, timing_events=ev)
+    ms, evs = timed(fn, steps, warmup, torch)
+    # candidate pairs only: each candidate sees its user's history and itself
+    pairs = 4 * sum(int(m) * (int(n) + 1) for n, m in zip(ci.hist_lens, ci.num_candidates))
+    flop = 4 * 128 * pairs
+    attn_ms = mean_span(evs, 1, 2)
+    kv_bytes = int(ci.hist_lens.sum()) * 4 * 128 * 2 * 2
+    return {
+        "workload": ci.name + "_paged_history",
+        "ms_per_step": round(ms, 4),
+        "attn_kernel_ms": round(attn_ms, 4),
+        "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+        "attn_kernel_tflops": round(flop / (attn_ms * 1e-3) / 1e12, 2),
+        "attn_kernel_kv_gbs": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1),
+        "algorithmic_gflop": round(flop / 1e9, 3),
+        "epilogue_ms": round(mean_span(evs, 2, 3), 4),
+        "scheduler_ms": round(mean_span(evs, 0, 1), 4),
+    }
+
+
 def bench_training_shape(torch, hs, W, steps, warmup):
     inp = W.training_shape()
     bf = torch.bfloat16
@@ -368,6 +410,7 @@ def main():
     if not args.no_variants:
         variants = {}
         for name, fn in (("kv_cache_delta", bench_cached), ("mfalcon", bench_mfalcon),
+                         ("mfalcon_paged_history", bench_mfalcon_paged),
                          ("jagged_training_shape", bench_training_shape), ("full_layer", bench_layer)):
             log(f"variant {name}")
             variants[name] = fn(torch, hs, W, args.steps, args.warmup)

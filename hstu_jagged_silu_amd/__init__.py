@@ -27,12 +27,13 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhstu.so")
 
 HSTU_F32, HSTU_BF16 = 0, 1
-HSTU_FN_FULL, HSTU_FN_CACHED, HSTU_FN_MFALCON = 0, 1, 2
+HSTU_FN_FULL, HSTU_FN_CACHED, HSTU_FN_MFALCON, HSTU_FN_MFALCON_CACHED = 0, 1, 2, 3
 PAGE_SIZE = 64
 
 EXPORTED_SYMBOLS = (
     "hstu_status_string", "hstu_version", "hstu_workspace_size", "hstu_attn_fwd",
-    "hstu_kv_append", "hstu_attn_fwd_cached", "hstu_mfalcon_fwd", "hstu_layer_workspace_size",
+    "hstu_kv_append", "hstu_attn_fwd_cached", "hstu_mfalcon_fwd", "hstu_mfalcon_fwd_cached",
+    "hstu_layer_workspace_size",
     "hstu_layer_fwd",
 )
 
@@ -86,6 +87,8 @@ def _load():
     lib.hstu_attn_fwd_cached.argtypes = [P, i32, vp, vp, i32, i32, i64, vp, vp, vp, K, vp, vp, sz, vp]
     lib.hstu_mfalcon_fwd.restype = ctypes.c_int
     lib.hstu_mfalcon_fwd.argtypes = [P, i32, vp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hstu_mfalcon_fwd_cached.restype = ctypes.c_int
+    lib.hstu_mfalcon_fwd_cached.argtypes = [P, i32, vp, vp, i32, i32, i64, vp, vp, vp, vp, vp, K, vp, vp, sz, vp]
     W = ctypes.POINTER(_LayerWeights)
     lib.hstu_layer_workspace_size.restype = sz
     lib.hstu_layer_workspace_size.argtypes = [P, i32, i32, i64, i32]
@@ -380,6 +383,34 @@ def hstu_attn_fwd_cached(q_new, u_new, ts_new, new_offsets, cache_lens, max_new:
                                      max_total, T, q_new.data_ptr(), u_new.data_ptr(), ts_new.data_ptr(),
                                      ctypes.byref(c), y.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
            "hstu_attn_fwd_cached")
+    return y
+
+
+def hstu_mfalcon_fwd_cached(q, k, v, u, ts, cand_offsets, hist_lens, max_cand: int, max_hist: int,
+                            cache: PagedKVCache, params: LayerParams, *, y=None, workspace=None,
+                            timing_events=None):
+    """Candidates score against the users' paged histories (hist_lens int32 [B])
+    and themselves. q, k, v: [T_cand, H, d]; u: [T_cand, H*d]; ts int64 [T_cand]."""
+    H, d = params.num_heads, params.head_dim
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _device_tensor(t, params.dtype, name)
+        if t.dim() != 3 or t.shape[1:] != (H, d):
+            raise ValueError(f"{name} must be [T, {H}, {d}]")
+    _device_tensor(u, params.dtype, "u")
+    _device_tensor(ts, torch.int64, "ts")
+    _device_tensor(cand_offsets, torch.int32, "cand_offsets")
+    _device_tensor(hist_lens, torch.int32, "hist_lens")
+    T, B = q.shape[0], cand_offsets.shape[0] - 1
+    y = torch.empty_like(u) if y is None else y
+    _device_tensor(y, params.dtype, "y")
+    nbytes = hstu_workspace_size(HSTU_FN_MFALCON_CACHED, params, B, T, max_hist)
+    ws = _workspace(workspace, nbytes, q.device)
+    c = cache.c_struct(params)
+    p = params.c_struct(timing_events)
+    _check(_lib.hstu_mfalcon_fwd_cached(ctypes.byref(p), B, cand_offsets.data_ptr(), hist_lens.data_ptr(),
+                                        max_cand, max_hist, T, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        u.data_ptr(), ts.data_ptr(), ctypes.byref(c), y.data_ptr(), ws.data_ptr(),
+                                        ws.numel(), _stream()), "hstu_mfalcon_fwd_cached")
     return y
 
 

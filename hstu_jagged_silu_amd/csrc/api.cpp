@@ -70,7 +70,7 @@ bool layout(int fn, const hstu_params_t* p, int32_t B, int64_t Tq, int64_t max_l
     w.max_items = H * tiles;
   } else if (fn == HSTU_FN_MFALCON) {
     w.max_items = H * (tiles + B);
-  } else if (fn == HSTU_FN_CACHED) {
+  } else if (fn == HSTU_FN_CACHED || fn == HSTU_FN_MFALCON_CACHED) {
     // splits actually used are ceil(max_len / chunk_keys) <= this bound, which
     // never decreases when max_len grows
     w.chunk_keys = chunk_keys_for(max_len);
@@ -333,10 +333,62 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_params_t* params, int32_t batch, c
   a.max_pages = cache->max_pages_per_seq;
   LnArgs l = ln_args(params, w, ws, u_new, y_new, total_new);
   l.chunk_keys = w.chunk_keys;
+  l.mode = MODE_CACHED;
   l.B = batch;
   l.offsets = new_offsets;
   l.cache_lens = cache_lens;
   return run_attention(params, s, a, MODE_CACHED, l, stream);
+}
+
+hstu_status_t hstu_mfalcon_fwd_cached(const hstu_params_t* params, int32_t batch, const int32_t* cand_offsets,
+                                      const int32_t* hist_lens, int32_t max_cand, int32_t max_hist,
+                                      int64_t total_cand, const void* q, const void* k, const void* v,
+                                      const void* u, const int64_t* ts, const hstu_kv_cache_t* cache, void* y,
+                                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  hstu_status_t st = check_params(params);
+  if (st != HSTU_OK) return st;
+  if (!cache) return HSTU_ERR_INVALID_ARG;
+  if (cache->page_size != PAGE) return HSTU_ERR_UNSUPPORTED;
+  if (batch < 0 || total_cand < 0 || max_cand < 0 || max_hist < 0 || cache->num_pages < 1 ||
+      cache->max_pages_per_seq < 1)
+    return HSTU_ERR_INVALID_ARG;
+  if (batch == 0 || total_cand == 0) return HSTU_OK;
+  if (any_null({cache->k_pages, cache->v_pages, cache->ts_pages, cache->page_table, cand_offsets, hist_lens, q,
+                k, v, u, ts, y}))
+    return HSTU_ERR_INVALID_ARG;
+  if (any_misaligned({cache->k_pages, cache->v_pages, cache->ts_pages, q, k, v, u, ts, y}))
+    return HSTU_ERR_INVALID_ARG;
+  if ((int64_t)cache->max_pages_per_seq * PAGE < max_hist) return HSTU_ERR_INVALID_ARG;
+  WsLayout w;
+  if (!layout(HSTU_FN_MFALCON_CACHED, params, batch, total_cand, max_hist, w)) return HSTU_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < w.total || !aligned16(ws)) return HSTU_ERR_WORKSPACE;
+
+  SchedArgs s = sched_args(MODE_MFALCON_PAGED, params, w, ws, batch, cand_offsets, w.chunk_keys);
+  s.cache_lens = hist_lens;
+  s.ts_pages = cache->ts_pages;
+  s.page_table = cache->page_table;
+  s.num_pages = cache->num_pages;
+  s.max_pages = cache->max_pages_per_seq;
+  AttnArgs a = base_args(params, w, ws, total_cand);
+  a.q = q;
+  a.k = k;  // candidates' own keys and values (the self term)
+  a.v = v;
+  a.ts = ts;
+  a.offsets = cand_offsets;
+  a.cache_lens = hist_lens;
+  a.k_pages = cache->k_pages;
+  a.v_pages = cache->v_pages;
+  a.ts_pages = cache->ts_pages;
+  a.page_table = cache->page_table;
+  a.num_pages = cache->num_pages;
+  a.max_pages = cache->max_pages_per_seq;
+  LnArgs l = ln_args(params, w, ws, u, y, total_cand);
+  l.chunk_keys = w.chunk_keys;
+  l.mode = MODE_MFALCON_PAGED;
+  l.B = batch;
+  l.offsets = cand_offsets;
+  l.cache_lens = hist_lens;
+  return run_attention(params, s, a, MODE_MFALCON_PAGED, l, stream);
 }
 
 }  // extern "C"

@@ -177,6 +177,12 @@ void attn_fwd_kernel(AttnArgs a) {
     kcount = C + Lq;
     pos0 = C + q_start;
     n_norm = C + Lq;
+  } else if (MODE == MODE_MFALCON_PAGED) {
+    const int C = ldc(a.cache_lens + b);  // history length; every row is a candidate at position C
+    kcount = C;
+    cand = true;
+    pos0 = C;
+    n_norm = C + 1;
   } else if (MODE == MODE_MFALCON) {
     const int n = Lq - ldc(a.num_cand + b);
     kcount = n;
@@ -259,7 +265,7 @@ void attn_fwd_kernel(AttnArgs a) {
     int64_t rstride;  // bytes between consecutive keys
     int nvalid = min(KT, kcount - j0);
     bool missing = false;
-    if (MODE == MODE_CACHED) {
+    if (mode_paged(MODE)) {
       int page = j0 / PAGE < a.max_pages ? ldc(a.page_table + (int64_t)b * a.max_pages + j0 / PAGE) : -1;
       if (page < 0 || page >= a.num_pages) {
         page = 0;
@@ -315,7 +321,7 @@ void attn_fwd_kernel(AttnArgs a) {
 
   // timestamp range of the keys of the tile at j0 (conservative superset)
   auto key_time_range = [&](int j0, int64_t& kmin, int64_t& kmax) {
-    if (MODE == MODE_CACHED) {
+    if (mode_paged(MODE)) {
       const int64_t blk = (int64_t)b * a.stat_stride + j0 / KT;
       kmin = ldc(a.tstats + 2 * blk);
       kmax = ldc(a.tstats + 2 * blk + 1);
@@ -577,7 +583,7 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   // ---- M-FALCON: a candidate's own key (relative position 0, dt = 0) -------
-  if (MODE == MODE_MFALCON && cand) {
+  if ((MODE == MODE_MFALCON || MODE == MODE_MFALCON_PAGED) && cand && it.chunk == 0) {
     const T* kp = (const T*)a.k + (qrow * H + h) * D;
     const T* vp = (const T*)a.v + (qrow * H + h) * D;
     float dot = 0.0f;
@@ -638,7 +644,8 @@ static hipError_t launch_mode(const AttnArgs& a, int mode, int64_t grid, hipStre
   dim3 g((unsigned)grid), blk(NTHREADS);
   if (mode == MODE_FULL) hipLaunchKernelGGL((attn_fwd_kernel<T, D, MODE_FULL>), g, blk, 0, s, a);
   else if (mode == MODE_CACHED) hipLaunchKernelGGL((attn_fwd_kernel<T, D, MODE_CACHED>), g, blk, 0, s, a);
-  else hipLaunchKernelGGL((attn_fwd_kernel<T, D, MODE_MFALCON>), g, blk, 0, s, a);
+  else if (mode == MODE_MFALCON) hipLaunchKernelGGL((attn_fwd_kernel<T, D, MODE_MFALCON>), g, blk, 0, s, a);
+  else hipLaunchKernelGGL((attn_fwd_kernel<T, D, MODE_MFALCON_PAGED>), g, blk, 0, s, a);
   return hipGetLastError();
 }
 

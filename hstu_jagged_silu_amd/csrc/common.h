@@ -13,8 +13,12 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 
-// Which attention variant a launch computes.
-enum Mode : int32_t { MODE_FULL = 0, MODE_CACHED = 1, MODE_MFALCON = 2 };
+// Which attention variant a launch computes. MODE_MFALCON_PAGED scores
+// candidates against a history held in the paged KV cache.
+enum Mode : int32_t { MODE_FULL = 0, MODE_CACHED = 1, MODE_MFALCON = 2, MODE_MFALCON_PAGED = 3 };
+
+// keys come from the page pool, and the cached path's key splits apply
+__host__ __device__ constexpr bool mode_paged(int m) { return m == MODE_CACHED || m == MODE_MFALCON_PAGED; }
 
 // Kinds of query tile: causal rows (full path, cached new tokens, M-FALCON
 // history) or M-FALCON candidate rows.

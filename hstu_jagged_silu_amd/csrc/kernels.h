@@ -73,8 +73,9 @@ struct LnArgs {
   float eps;
   int32_t HD;
   int64_t T;
-  // split bookkeeping (cached path); chunk_keys == 0 means one split
+  // split bookkeeping (paged paths); chunk_keys == 0 means one split
   int32_t chunk_keys;
+  int32_t mode;                  // MODE_CACHED or MODE_MFALCON_PAGED when chunk_keys > 0
   int32_t n_chunks;
   int32_t B;
   const int32_t* offsets;

@@ -60,8 +60,11 @@ __global__ __launch_bounds__(64 * LN_ROWS) void ln_gate_kernel(LnArgs a) {
     const int b = lo;
     const int m = (int)(row - a.offsets[b]);
     const int Lb = a.offsets[b + 1] - a.offsets[b];
-    const int kend = a.cache_lens[b] + min((m / QT + 1) * QT, Lb);
-    nsplit = min((int)ceil_div(kend, a.chunk_keys), a.n_chunks);
+    // keys seen by the work item that holds this row: causal new tokens end at
+    // their tile's last row; paged candidates see the whole history
+    const int kend = a.mode == MODE_MFALCON_PAGED ? a.cache_lens[b]
+                                                  : a.cache_lens[b] + min((m / QT + 1) * QT, Lb);
+    nsplit = max(1, min((int)ceil_div(kend, a.chunk_keys), a.n_chunks));
   }
 
   bool on[NCH];

@@ -30,7 +30,7 @@ struct UserGeo {
 __device__ inline UserGeo user_geo(const SchedArgs& a, int b) {
   UserGeo g;
   g.L = max(0, a.offsets[b + 1] - a.offsets[b]);
-  g.C = (a.mode == MODE_CACHED) ? a.cache_lens[b] : 0;
+  g.C = mode_paged(a.mode) ? a.cache_lens[b] : 0;
   g.n = g.L;
   g.nq_cand = 0;
   if (a.mode == MODE_MFALCON) {
@@ -39,6 +39,11 @@ __device__ inline UserGeo user_geo(const SchedArgs& a, int b) {
     g.nq_cand = (int)ceil_div(m, QT);
   }
   g.nq_causal = (int)ceil_div(g.n, QT);
+  if (a.mode == MODE_MFALCON_PAGED) {  // every row is a candidate; the history is C
+    g.n = 0;
+    g.nq_causal = 0;
+    g.nq_cand = (int)ceil_div(g.L, QT);
+  }
   return g;
 }
 
@@ -49,7 +54,14 @@ __device__ inline int tile_chunks(const SchedArgs& a, const UserGeo& g, int qt) 
   return (int)ceil_div(kend, a.chunk_keys);
 }
 
+// key splits of every candidate tile on the paged M-FALCON path (at least one,
+// which carries the candidates' own keys when the history is empty)
+__device__ inline int cand_chunks(const SchedArgs& a, const UserGeo& g) {
+  return max(1, (int)ceil_div(g.C, a.chunk_keys));
+}
+
 __device__ inline int user_items_per_head(const SchedArgs& a, const UserGeo& g) {
+  if (a.mode == MODE_MFALCON_PAGED) return g.nq_cand * cand_chunks(a, g);
   if (a.mode != MODE_CACHED) return g.nq_causal + g.nq_cand;
   int s = 0;
   for (int qt = 0; qt < g.nq_causal; ++qt) s += tile_chunks(a, g, qt);
@@ -66,7 +78,16 @@ __device__ inline WorkItem make_item(const SchedArgs& a, int b, int local) {
   int t = local % per_head;
   w.chunk = 0;
   w.kind = KIND_CAUSAL;
-  if (a.mode == MODE_CACHED) {
+  if (a.mode == MODE_MFALCON_PAGED) {
+    const int nc = cand_chunks(a, g);
+    const int qt = t / nc;
+    w.kind = KIND_CANDIDATE;
+    w.chunk = t % nc;
+    w.q_start = qt * QT;
+    w.q_len = min(QT, g.L - w.q_start);
+    w.k_begin = min(w.chunk * a.chunk_keys, g.C);
+    w.k_end = min(g.C, (w.chunk + 1) * a.chunk_keys);
+  } else if (a.mode == MODE_CACHED) {
     int qt = 0;
     while (t >= tile_chunks(a, g, qt)) { t -= tile_chunks(a, g, qt); ++qt; }
     w.q_start = qt * QT;
@@ -124,9 +145,9 @@ __device__ void key_time_ranges(const SchedArgs& a) {
   if (blk >= a.n_stat_blocks) return;
   bool ok;
   int64_t v = 0;
-  if (a.mode == MODE_CACHED) {
+  if (mode_paged(a.mode)) {
     const int b = (int)(blk / a.stat_stride), kt = (int)(blk % a.stat_stride);
-    const int kcount = a.cache_lens[b] + (a.offsets[b + 1] - a.offsets[b]);
+    const int kcount = a.cache_lens[b] + (a.mode == MODE_CACHED ? a.offsets[b + 1] - a.offsets[b] : 0);
     const int page = kt < a.max_pages ? a.page_table[(int64_t)b * a.max_pages + kt] : -1;
     ok = kt * KT + lane < kcount && page >= 0 && page < a.num_pages;
     if (ok) v = a.ts_pages[(int64_t)page * PAGE + lane];

@@ -71,7 +71,12 @@ typedef enum {
 typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype_t;
 
 /* Which entry point a workspace is sized for. */
-typedef enum { HSTU_FN_FULL = 0, HSTU_FN_CACHED = 1, HSTU_FN_MFALCON = 2 } hstu_fn_t;
+typedef enum {
+  HSTU_FN_FULL = 0,
+  HSTU_FN_CACHED = 1,
+  HSTU_FN_MFALCON = 2,
+  HSTU_FN_MFALCON_CACHED = 3
+} hstu_fn_t;
 
 /*
  * Layer parameters shared by every attention entry point.
@@ -218,6 +223,34 @@ hstu_status_t hstu_mfalcon_fwd(const hstu_params_t* params, int32_t batch, const
                                const void* q, const void* k, const void* v, const void* u,
                                const int64_t* ts, void* y, void* ws, size_t ws_bytes,
                                hipStream_t stream);
+
+/*
+ * M-FALCON over a paged history: the candidates of user b (packed rows
+ * cand_offsets[b] .. cand_offsets[b+1]) are scored against the user's
+ * n_b = hist_lens[b] history tokens already in the paged cache ("HSTU
+ * Generative Recommenders: Deploy on GPU Cloud", section "M-FALCON:
+ * Microbatched Attention for Scoring Multiple Candidates at Once", with the
+ * history kept in the paged GPU table of page "recomendador-generativo-hstu-
+ * dynamo-triton", section "Como o recomendador generativo HSTU reutiliza o
+ * histórico"). Every candidate sits at position n_b, attends to history keys
+ * 0 .. n_b - 1 (read from the pages, relative position n_b - j) and to
+ * itself (relative position 0, time difference 0), and to no other
+ * candidate; N_b = n_b + 1. Each output row therefore equals the candidate's
+ * row of hstu_mfalcon_fwd on [history | candidates].
+ *   cand_offsets      int32 [batch + 1] over the packed candidate rows
+ *   hist_lens         int32 [batch], history tokens in the cache (may be 0)
+ *   max_cand          >= every candidate count; max_hist >= every n_b
+ *   q, k, v           [T_cand, H, d] candidates' own query, key, value rows
+ *   u, y              [T_cand, H*d]; ts int64 [T_cand] candidate timestamps
+ *   ws                hstu_workspace_size(HSTU_FN_MFALCON_CACHED, params,
+ *                     batch, T_cand, max_hist) bytes
+ * Nothing is appended to the cache: candidates are scored, not stored.
+ */
+hstu_status_t hstu_mfalcon_fwd_cached(const hstu_params_t* params, int32_t batch, const int32_t* cand_offsets,
+                                      const int32_t* hist_lens, int32_t max_cand, int32_t max_hist,
+                                      int64_t total_cand, const void* q, const void* k, const void* v,
+                                      const void* u, const int64_t* ts, const hstu_kv_cache_t* cache, void* y,
+                                      void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Full HSTU layer ("How Generative Recommenders Are Redefining RecSys at

@@ -109,6 +109,8 @@ def test_workspace_size_valid_and_invalid():
     cached = _ws(1, p, 8, 1024, 8320)
     assert cached >= 1024 * 512 * 4 * 2                    # at least two key splits of O
     assert _ws(2, p, 4, 20480, 5120) >= 20480 * 512 * 4
+    assert _ws(3, p, 4, 4096, 4096) >= 4096 * 512 * 4 * 8  # paged M-FALCON: eight key splits of O
+    assert _ws(3, p, 4, 4096, 4097) >= _ws(3, p, 4, 4096, 4096)
     assert _ws(7, p, 8, 1024, 1024) == 0                   # unknown entry point
     assert _ws(0, _params(dtype=5), 8, 1024, 128) == 0      # unknown dtype
     assert _ws(0, _params(head_dim=48), 8, 1024, 128) == 0  # unsupported head dim
@@ -201,6 +203,29 @@ def test_layer_workspace_and_bad_arguments_before_launch():
     assert call(_params(head_dim=48)) == INVALID
     assert call(p) == WORKSPACE
     assert call(p, B=0) == OK
+
+
+def test_paged_mfalcon_rejects_bad_arguments_before_launch():
+    lib = hs.lib()
+    c = hs._KVCache()
+    c.k_pages = c.v_pages = c.ts_pages = c.page_table = FAKE
+    c.num_pages, c.page_size, c.max_pages_per_seq = 10, 64, 4
+    p = _params()
+    f = lib.hstu_mfalcon_fwd_cached
+
+    def call(p=p, c=c, B=2, T=32, max_hist=200, q=FAKE, wsb=0):
+        return f(ctypes.byref(p), B, FAKE, FAKE, 16, max_hist, T, q, FAKE, FAKE, FAKE, FAKE, ctypes.byref(c), FAKE,
+                 FAKE, wsb, None)
+
+    assert call() == WORKSPACE
+    assert call(max_hist=4 * 64 + 1, wsb=1 << 40) == INVALID   # history beyond the page table
+    assert call(q=None, wsb=1 << 40) == INVALID
+    assert call(q=FAKE + 8, wsb=1 << 40) == INVALID
+    assert call(p=_params(head_dim=48)) == UNSUPPORTED
+    assert call(B=0) == OK
+    assert call(T=0) == OK
+    c.page_size = 32
+    assert call(wsb=1 << 40) == UNSUPPORTED
 
 
 def test_pair_count_matches_closed_forms():

@@ -239,6 +239,33 @@ class CandidateInputs:
     hist_lens: np.ndarray        # int32 [B]
     num_candidates: np.ndarray   # int32 [B]
 
+    def split(self):
+        """Packed (history rows, candidate rows) index arrays into ``inputs``."""
+        off = self.inputs.seq_offsets
+        hist, cand = [], []
+        for b in range(len(self.hist_lens)):
+            s = int(off[b])
+            n, m = int(self.hist_lens[b]), int(self.num_candidates[b])
+            hist.append(np.arange(s, s + n))
+            cand.append(np.arange(s + n, s + n + m))
+        cat = lambda xs: np.concatenate(xs) if xs else np.zeros(0, np.int64)
+        return cat(hist).astype(np.int64), cat(cand).astype(np.int64)
+
+    def history_pages(self, seed: int, page_size: int = 64, spare_pages: int = 16):
+        """A page pool for the histories: (num_pages, page_table [B, max_pages]),
+        pages drawn as a seeded permutation of the pool, -1 = unused."""
+        rng = np.random.default_rng(seed)
+        pages_per = [(int(n) + page_size - 1) // page_size for n in self.hist_lens]
+        max_pages = max([1] + pages_per)
+        num_pages = int(sum(pages_per)) + spare_pages
+        perm = rng.permutation(num_pages).astype(np.int32)
+        table = np.full((len(self.hist_lens), max_pages), -1, dtype=np.int32)
+        p = 0
+        for b, n in enumerate(pages_per):
+            table[b, :n] = perm[p:p + n]
+            p += n
+        return num_pages, table
+
 
 def candidates(name, seed, hist_lens, cand_lens, H=4, d=128, dtype="bf16", n_pos=128, n_time=128):
     rng = np.random.default_rng(seed)
