@@ -34,7 +34,8 @@ EXPORTED_SYMBOLS = (
     "hstu_status_string", "hstu_version", "hstu_workspace_size", "hstu_attn_fwd",
     "hstu_kv_append", "hstu_attn_fwd_cached", "hstu_mfalcon_fwd", "hstu_mfalcon_fwd_cached",
     "hstu_layer_workspace_size",
-    "hstu_layer_fwd",
+    "hstu_layer_fwd", "hstu_pm_create", "hstu_pm_destroy", "hstu_pm_reserve", "hstu_pm_commit", "hstu_pm_lookup",
+    "hstu_pm_evict", "hstu_pm_stats",
 )
 
 
@@ -89,6 +90,20 @@ def _load():
     lib.hstu_mfalcon_fwd.argtypes = [P, i32, vp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hstu_mfalcon_fwd_cached.restype = ctypes.c_int
     lib.hstu_mfalcon_fwd_cached.argtypes = [P, i32, vp, vp, i32, i32, i64, vp, vp, vp, vp, vp, K, vp, vp, sz, vp]
+    lib.hstu_pm_create.restype = vp
+    lib.hstu_pm_create.argtypes = [i32, i32, i32]
+    lib.hstu_pm_destroy.restype = None
+    lib.hstu_pm_destroy.argtypes = [vp]
+    lib.hstu_pm_reserve.restype = ctypes.c_int
+    lib.hstu_pm_reserve.argtypes = [vp, i32, vp, vp, vp, vp, ctypes.POINTER(i32)]
+    lib.hstu_pm_commit.restype = ctypes.c_int
+    lib.hstu_pm_commit.argtypes = [vp, i32, vp, vp]
+    lib.hstu_pm_lookup.restype = i32
+    lib.hstu_pm_lookup.argtypes = [vp, i64]
+    lib.hstu_pm_evict.restype = ctypes.c_int
+    lib.hstu_pm_evict.argtypes = [vp, i64]
+    lib.hstu_pm_stats.restype = ctypes.c_int
+    lib.hstu_pm_stats.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i64)]
     W = ctypes.POINTER(_LayerWeights)
     lib.hstu_layer_workspace_size.restype = sz
     lib.hstu_layer_workspace_size.argtypes = [P, i32, i32, i64, i32]
@@ -412,6 +427,58 @@ def hstu_mfalcon_fwd_cached(q, k, v, u, ts, cand_offsets, hist_lens, max_cand: i
                                         u.data_ptr(), ts.data_ptr(), ctypes.byref(c), y.data_ptr(), ws.data_ptr(),
                                         ws.numel(), _stream()), "hstu_mfalcon_fwd_cached")
     return y
+
+
+class PageManager:
+    """Host-side page manager of the paged KV cache (hstu_pm_*): which pool
+    pages hold which user's history, with LRU eviction. Page ids only; the
+    bytes live in PagedKVCache pools (one per layer, same page ids)."""
+
+    def __init__(self, num_pages: int, max_pages_per_seq: int, max_users: int):
+        self._h = _lib.hstu_pm_create(num_pages, max_pages_per_seq, max_users)
+        if not self._h:
+            raise HstuError("hstu_pm_create: invalid arguments")
+        self.num_pages, self.max_pages_per_seq, self.max_users = num_pages, max_pages_per_seq, max_users
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            try:
+                _lib.hstu_pm_destroy(h)
+            except Exception:  # interpreter shutdown
+                pass
+            self._h = None
+
+    def reserve(self, user_ids, n_new):
+        """Returns (cache_lens int32 [B], page_table int32 [B, max_pages], evicted)."""
+        import numpy as np
+        ids = np.ascontiguousarray(user_ids, dtype=np.int64)
+        n = np.ascontiguousarray(n_new, dtype=np.int32)
+        if ids.shape != n.shape or ids.ndim != 1:
+            raise ValueError("user_ids and n_new must be 1-D of equal length")
+        lens = np.zeros(len(ids), np.int32)
+        table = np.full((len(ids), self.max_pages_per_seq), -1, np.int32)
+        ev = ctypes.c_int32(0)
+        _check(_lib.hstu_pm_reserve(self._h, len(ids), ids.ctypes.data, n.ctypes.data, lens.ctypes.data,
+                                    table.ctypes.data, ctypes.byref(ev)), "hstu_pm_reserve")
+        return lens, table, int(ev.value)
+
+    def commit(self, user_ids, n_new):
+        import numpy as np
+        ids = np.ascontiguousarray(user_ids, dtype=np.int64)
+        n = np.ascontiguousarray(n_new, dtype=np.int32)
+        _check(_lib.hstu_pm_commit(self._h, len(ids), ids.ctypes.data, n.ctypes.data), "hstu_pm_commit")
+
+    def lookup(self, user_id: int) -> int:
+        return int(_lib.hstu_pm_lookup(self._h, int(user_id)))
+
+    def evict(self, user_id: int):
+        _check(_lib.hstu_pm_evict(self._h, int(user_id)), "hstu_pm_evict")
+
+    def stats(self):
+        fp, us, ev = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int64(0)
+        _check(_lib.hstu_pm_stats(self._h, ctypes.byref(fp), ctypes.byref(us), ctypes.byref(ev)), "hstu_pm_stats")
+        return {"free_pages": fp.value, "users": us.value, "evictions": ev.value}
 
 
 class HipEvent:

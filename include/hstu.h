@@ -253,6 +253,51 @@ hstu_status_t hstu_mfalcon_fwd_cached(const hstu_params_t* params, int32_t batch
                                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Page manager of the paged KV cache (host side). It decides which pages of a
+ * pool of num_pages hold which user's history and evicts the least recently
+ * used users when the pool or the user slots run out: the lookup / allocate /
+ * append / evict operations of the paged GPU table on page
+ * "recomendador-generativo-hstu-dynamo-triton", section "Como o recomendador
+ * generativo HSTU reutiliza o histórico". It moves page ids only: the K, V and
+ * timestamp bytes stay in the device pools that hstu_kv_append writes. One
+ * manager serves every layer of a model (each layer has its own pools indexed
+ * by the same page ids). All functions are host-only, thread-safe, and never
+ * touch the GPU. Users are 64-bit ids; pages hold 64 tokens.
+ *
+ * A serving step for a batch of users:
+ *   1. hstu_pm_reserve(batch ids, new token counts) -> each user's cached
+ *      length before this step and its page-table row ([batch,
+ *      max_pages_per_seq] int32, -1 = none), with pages added for the new
+ *      tokens; copy both to the device. A user evicted earlier (or never seen)
+ *      comes back with cached length 0: the caller sends its whole history.
+ *   2. per layer: hstu_kv_append, then hstu_attn_fwd_cached.
+ *   3. hstu_pm_commit(batch ids, new token counts) advances the lengths.
+ * Every lookup, and every user of a reserve in batch order, counts as a use;
+ * eviction takes the least recently used user outside the request. Users of
+ * the batch are never evicted by their own reserve. A reserve that
+ * cannot fit even after evicting every other user returns
+ * HSTU_ERR_WORKSPACE and changes nothing; a user whose history would exceed
+ * max_pages_per_seq pages gives HSTU_ERR_UNSUPPORTED; duplicate ids in one
+ * call give HSTU_ERR_INVALID_ARG.
+ */
+typedef struct hstu_page_manager hstu_page_manager_t;
+
+/* NULL when an argument is < 1 or memory runs out. */
+hstu_page_manager_t* hstu_pm_create(int32_t num_pages, int32_t max_pages_per_seq, int32_t max_users);
+void hstu_pm_destroy(hstu_page_manager_t* pm);
+/* cache_lens: [batch] out; page_table: [batch, max_pages_per_seq] out; evicted: users evicted (may be NULL) */
+hstu_status_t hstu_pm_reserve(hstu_page_manager_t* pm, int32_t batch, const int64_t* user_ids,
+                              const int32_t* n_new, int32_t* cache_lens, int32_t* page_table, int32_t* evicted);
+hstu_status_t hstu_pm_commit(hstu_page_manager_t* pm, int32_t batch, const int64_t* user_ids,
+                             const int32_t* n_new);
+/* cached length of a user (marks it recently used), or -1 when not resident */
+int32_t hstu_pm_lookup(hstu_page_manager_t* pm, int64_t user_id);
+/* drop a resident user and free its pages; HSTU_ERR_INVALID_ARG if absent */
+hstu_status_t hstu_pm_evict(hstu_page_manager_t* pm, int64_t user_id);
+/* free pages, resident users, evictions so far (each may be NULL) */
+hstu_status_t hstu_pm_stats(hstu_page_manager_t* pm, int32_t* free_pages, int32_t* users, int64_t* evictions);
+
+/*
  * Full HSTU layer ("How Generative Recommenders Are Redefining RecSys at
  * Scale", Takeaways: elementwise gating before the output projection;
  * "Generative recommenders at scale", section "Inside NVIDIA's GPU-native
