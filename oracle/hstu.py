@@ -60,6 +60,7 @@ __all__ = [
     "time_bucket", "pos_bucket", "silu", "layer_norm_gate",
     "hstu_full", "hstu_full_rows", "hstu_cached", "hstu_mfalcon",
     "kv_append_pages", "hstu_layer", "max_rel_row_error", "pair_count",
+    "silu_grad", "layer_norm_gate_bwd", "hstu_full_bwd",
 ]
 
 
@@ -375,6 +376,111 @@ def hstu_layer(x, w1, w2, ts, seq_offsets, num_heads, head_dim, pos_tab=None, ti
                            gamma, beta, eps)
         out[sel] = y @ np.asarray(w2, dtype=np.float64)
     return out
+
+
+# ----------------------------------------------------------------------------
+# Backward of the full causal path (training)
+# ----------------------------------------------------------------------------
+#
+# Training is the pages' other workload ("HSTU Generative Recommenders: Deploy
+# on GPU Cloud", section "Scaling Training and Serving Across Multiple GPUs";
+# "Generative recommenders at scale", section "Inside NVIDIA's GPU-native stack
+# for HSTU and Semantic IDs": model FLOP utilisation of HSTU training). The
+# pages print no backward formula; the gradients below are the chain rule of
+# the forward definition at the top of this module, written out step by step.
+
+def silu_grad(x):
+    """d SiLU(x) / dx = sigma(x) * (1 + x * (1 - sigma(x))) in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        sg = 1.0 / (1.0 + np.exp(-x))
+    return sg * (1.0 + x * (1.0 - sg))
+
+
+def layer_norm_gate_bwd(z, u, dy, gamma=None, beta=None, eps=1e-5):
+    """Gradients of y = ((z - mean) / sqrt(var + eps) * gamma + beta) * u, per token.
+
+    Returns (dz, du, dgamma, dbeta); dgamma and dbeta are None when gamma or
+    beta is None. With n = (z - mean) * r, r = 1 / sqrt(var + eps) and
+    g = dy * u * gamma (the gradient reaching n), the population-variance
+    normalisation gives dz = r * (g - mean(g) - n * mean(g * n)).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    mu = z.mean(axis=-1, keepdims=True)
+    var = ((z - mu) ** 2).mean(axis=-1, keepdims=True)
+    r = 1.0 / np.sqrt(var + eps)
+    n = (z - mu) * r
+    gam = np.ones(z.shape[-1]) if gamma is None else np.asarray(gamma, dtype=np.float64)
+    bet = np.zeros(z.shape[-1]) if beta is None else np.asarray(beta, dtype=np.float64)
+    du = dy * (n * gam + bet)
+    dn_aff = dy * u                       # gradient reaching n * gamma + beta
+    dgamma = None if gamma is None else (dn_aff * n).sum(axis=0)
+    dbeta = None if beta is None else dn_aff.sum(axis=0)
+    g = dn_aff * gam
+    dz = r * (g - g.mean(axis=-1, keepdims=True) - n * (g * n).mean(axis=-1, keepdims=True))
+    return dz, du, dgamma, dbeta
+
+
+def hstu_full_bwd(q, k, v, u, ts, seq_offsets, dy, pos_tab=None, time_tab=None, alpha=1.0, norm_n=0,
+                  gamma=None, beta=None, eps=1e-5):
+    """Gradients of the full causal path (hstu_full) for an upstream gradient dy [T, H*d].
+
+    Per sequence and head, with s = alpha q k^T + bias, a = SiLU(s) / N on
+    allowed pairs and o = a v:
+        da = do v^T,   dv = a^T do,
+        ds = da * SiLU'(s) / N on allowed pairs (0 elsewhere),
+        dq = alpha ds k,   dk = alpha ds^T q,
+        dP[c] = sum of ds over pairs whose position bucket is c,
+        dT[c] = sum of ds over pairs whose time bucket is c,
+    a shared (1-D) table summing over heads, a per-head ([H, n]) table per row.
+    The norm and gating gradients come from layer_norm_gate_bwd.
+    Returns a dict with dq, dk, dv ([T, H, d]), du ([T, H*d]), dpos, dtime
+    (shaped like the tables, None without one), dgamma, dbeta.
+    """
+    H, d = _heads(q)
+    T = q.shape[0]
+    off = np.asarray(seq_offsets, dtype=np.int64)
+    _, o = hstu_full(q, k, v, u, ts, off, pos_tab, time_tab, alpha, norm_n, gamma, beta, eps)
+    do, du, dgamma, dbeta = layer_norm_gate_bwd(o, u, dy, gamma, beta, eps)
+    do = do.reshape(T, H, d)
+    dq = np.zeros((T, H, d))
+    dk = np.zeros((T, H, d))
+    dv = np.zeros((T, H, d))
+    dpos = None if pos_tab is None else np.zeros(np.shape(pos_tab))
+    dtime = None if time_tab is None else np.zeros(np.shape(time_tab))
+    for b in range(len(off) - 1):
+        s0, s1 = int(off[b]), int(off[b + 1])
+        L = s1 - s0
+        if L == 0:
+            continue
+        pos = np.arange(L)
+        allowed = pos[None, :] <= pos[:, None]
+        n_norm = norm_n if norm_n > 0 else L
+        rel = np.where(allowed, pos[:, None] - pos[None, :], 0)
+        t = np.asarray(ts[s0:s1], dtype=np.int64)
+        dt = t[:, None] - t[None, :]
+        for h in range(H):
+            qh = np.asarray(q[s0:s1, h], dtype=np.float64)
+            kh = np.asarray(k[s0:s1, h], dtype=np.float64)
+            vh = np.asarray(v[s0:s1, h], dtype=np.float64)
+            s = alpha * (qh @ kh.T) + _bias(rel, dt, pos_tab, time_tab, h)
+            a = np.where(allowed, silu(s), 0.0) / float(n_norm)
+            doh = do[s0:s1, h]
+            dv[s0:s1, h] = a.T @ doh
+            da = doh @ vh.T
+            ds = np.where(allowed, da * silu_grad(s), 0.0) / float(n_norm)
+            dq[s0:s1, h] = alpha * (ds @ kh)
+            dk[s0:s1, h] = alpha * (ds.T @ qh)
+            if dpos is not None:
+                row = dpos if dpos.ndim == 1 else dpos[h]
+                np.add.at(row, pos_bucket(rel[allowed], row.shape[0]), ds[allowed])
+            if dtime is not None:
+                row = dtime if dtime.ndim == 1 else dtime[h]
+                np.add.at(row, time_bucket(dt[allowed], row.shape[0]), ds[allowed])
+    return {"dq": dq, "dk": dk, "dv": dv, "du": du, "dpos": dpos, "dtime": dtime,
+            "dgamma": dgamma, "dbeta": dbeta}
 
 
 # ----------------------------------------------------------------------------
