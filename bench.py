@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PMC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_causal_B8_L8192_H4_d128_traffic.json")
-KERNEL_SOURCES = ("attn_fwd.hip", "common.h", "kernels.h")
+KERNEL_SOURCES = ("attn_fwd.hip", "tile.h", "common.h", "kernels.h")
 
 
 def log(*a):

@@ -27,12 +27,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhstu.so")
 
 HSTU_F32, HSTU_BF16 = 0, 1
-HSTU_FN_FULL, HSTU_FN_CACHED, HSTU_FN_MFALCON, HSTU_FN_MFALCON_CACHED = 0, 1, 2, 3
+HSTU_FN_FULL, HSTU_FN_CACHED, HSTU_FN_MFALCON, HSTU_FN_MFALCON_CACHED, HSTU_FN_FULL_BWD = 0, 1, 2, 3, 4
 PAGE_SIZE = 64
 
 EXPORTED_SYMBOLS = (
     "hstu_status_string", "hstu_version", "hstu_workspace_size", "hstu_attn_fwd",
-    "hstu_kv_append", "hstu_attn_fwd_cached", "hstu_mfalcon_fwd", "hstu_mfalcon_fwd_cached",
+    "hstu_kv_append", "hstu_attn_fwd_cached", "hstu_mfalcon_fwd", "hstu_mfalcon_fwd_cached", "hstu_attn_bwd",
     "hstu_layer_workspace_size",
     "hstu_layer_fwd", "hstu_pm_create", "hstu_pm_destroy", "hstu_pm_reserve", "hstu_pm_commit", "hstu_pm_lookup",
     "hstu_pm_evict", "hstu_pm_stats",
@@ -62,6 +62,12 @@ class _KVCache(ctypes.Structure):
     ]
 
 
+class _Grads(ctypes.Structure):
+    _fields_ = [("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p), ("du", ctypes.c_void_p),
+                ("d_pos_tab", ctypes.c_void_p), ("d_time_tab", ctypes.c_void_p), ("d_ln_w", ctypes.c_void_p),
+                ("d_ln_b", ctypes.c_void_p)]
+
+
 class _LayerWeights(ctypes.Structure):
     _fields_ = [("embed_dim", ctypes.c_int32), ("w1", ctypes.c_void_p), ("w2", ctypes.c_void_p)]
 
@@ -82,6 +88,8 @@ def _load():
     lib.hstu_workspace_size.argtypes = [i32, P, i32, i64, i32]
     lib.hstu_attn_fwd.restype = ctypes.c_int
     lib.hstu_attn_fwd.argtypes = [P, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hstu_attn_bwd.restype = ctypes.c_int
+    lib.hstu_attn_bwd.argtypes = [P, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(_Grads), vp, sz, vp]
     lib.hstu_kv_append.restype = ctypes.c_int
     lib.hstu_kv_append.argtypes = [K, P, i32, vp, vp, i64, vp, vp, vp, vp]
     lib.hstu_attn_fwd_cached.restype = ctypes.c_int
@@ -259,6 +267,34 @@ def hstu_attn_fwd(q, k, v, u, ts, seq_offsets, max_len: int, params: LayerParams
                               v.data_ptr(), u.data_ptr(), ts.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(),
                               _stream()), "hstu_attn_fwd")
     return y
+
+
+def hstu_attn_bwd(q, k, v, u, ts, seq_offsets, max_len: int, dy, params: LayerParams, *, workspace=None,
+                  timing_events=None, table_grads: bool = True, affine_grads: bool = True):
+    """Backward of hstu_attn_fwd for the upstream gradient dy [T, H*d].
+
+    Returns a dict with dq, dk, dv ([T, H, d], bf16), du ([T, H*d], bf16),
+    d_pos_tab / d_time_tab (fp32, shaped like the tables; None without a
+    table or when table_grads is False) and d_ln_w / d_ln_b (fp32 [H*d]; None
+    without the affine term or when affine_grads is False)."""
+    _jagged_checks(params, q, k, v, u, ts, seq_offsets)
+    _device_tensor(dy, params.dtype, "dy")
+    if dy.shape != u.shape:
+        raise ValueError("dy must have the shape of u")
+    T, B = q.shape[0], seq_offsets.shape[0] - 1
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v), "du": torch.empty_like(u)}
+    for name, src, want in (("d_pos_tab", params.pos_tab, table_grads), ("d_time_tab", params.time_tab, table_grads),
+                            ("d_ln_w", params.ln_w, affine_grads), ("d_ln_b", params.ln_b, affine_grads)):
+        out[name] = torch.empty_like(src) if (src is not None and want) else None
+    g = _Grads(out["dq"].data_ptr(), out["dk"].data_ptr(), out["dv"].data_ptr(), out["du"].data_ptr(),
+               _ptr(out["d_pos_tab"]), _ptr(out["d_time_tab"]), _ptr(out["d_ln_w"]), _ptr(out["d_ln_b"]))
+    nbytes = hstu_workspace_size(HSTU_FN_FULL_BWD, params, B, T, max_len)
+    ws = _workspace(workspace, nbytes, q.device)
+    p = params.c_struct(timing_events)
+    _check(_lib.hstu_attn_bwd(ctypes.byref(p), B, seq_offsets.data_ptr(), max_len, T, q.data_ptr(), k.data_ptr(),
+                              v.data_ptr(), u.data_ptr(), ts.data_ptr(), dy.data_ptr(), ctypes.byref(g),
+                              ws.data_ptr(), ws.numel(), _stream()), "hstu_attn_bwd")
+    return out
 
 
 def hstu_mfalcon_fwd(q, k, v, u, ts, seq_offsets, num_candidates, max_len: int, params: LayerParams, *, y=None,

@@ -66,7 +66,7 @@ bool layout(int fn, const hstu_params_t* p, int32_t B, int64_t Tq, int64_t max_l
   w.chunk_keys = 0;
   w.stat_stride = 0;
   w.n_stat_blocks = ceil_div(Tq, KT);           // jagged keys: packed 64-row blocks
-  if (fn == HSTU_FN_FULL) {
+  if (fn == HSTU_FN_FULL || fn == HSTU_FN_FULL_BWD) {
     w.max_items = H * tiles;
   } else if (fn == HSTU_FN_MFALCON) {
     w.max_items = H * (tiles + B);
@@ -87,6 +87,16 @@ bool layout(int fn, const hstu_params_t* p, int32_t B, int64_t Tq, int64_t max_l
   w.stats_off = align_up(w.scratch_off + (size_t)(B + 1) * sizeof(int32_t));
   w.o_off = align_up(w.stats_off + (size_t)w.n_stat_blocks * 2 * sizeof(int64_t));
   w.total = align_up(w.o_off + (size_t)w.n_chunks * (size_t)Tq * (size_t)HD * sizeof(float));
+  w.dout_off = w.rab_off = w.lnp_off = w.total;
+  w.ln_waves = 0;
+  if (fn == HSTU_FN_FULL_BWD) {
+    const bool tables = p->pos_tab || p->time_tab;
+    const bool affine = p->ln_w || p->ln_b;
+    w.ln_waves = (int32_t)std::min<int64_t>(ceil_div(Tq, 8), 2048);
+    w.rab_off = align_up(w.dout_off + (size_t)Tq * (size_t)HD * 2);
+    w.lnp_off = align_up(w.rab_off + (tables ? (size_t)w.max_items * RAB_SLOTS * sizeof(float) : 0));
+    w.total = align_up(w.lnp_off + (affine ? (size_t)2 * w.ln_waves * (size_t)HD * sizeof(float) : 0));
+  }
   return true;
 }
 
@@ -224,6 +234,115 @@ hstu_status_t hstu_attn_fwd(const hstu_params_t* params, int32_t batch, const in
   a.offsets = seq_offsets;
   LnArgs l = ln_args(params, w, ws, u, y, total_tokens);
   return run_attention(params, s, a, MODE_FULL, l, stream);
+}
+
+hstu_status_t hstu_attn_bwd(const hstu_params_t* params, int32_t batch, const int32_t* seq_offsets,
+                            int32_t max_len, int64_t total_tokens, const void* q, const void* k,
+                            const void* v, const void* u, const int64_t* ts, const void* dy,
+                            const hstu_grads_t* grads, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hstu_status_t st = check_params(params);
+  if (st != HSTU_OK) return st;
+  if (params->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
+  if (params->pos_tab && params->n_pos > BWD_MAX_NPOS) return HSTU_ERR_UNSUPPORTED;
+  if (batch < 0 || total_tokens < 0 || max_len < 0 || !grads) return HSTU_ERR_INVALID_ARG;
+  if ((grads->d_pos_tab && !params->pos_tab) || (grads->d_time_tab && !params->time_tab) ||
+      (grads->d_ln_w && !params->ln_w) || (grads->d_ln_b && !params->ln_b))
+    return HSTU_ERR_INVALID_ARG;
+  if (any_misaligned({grads->d_ln_w, grads->d_ln_b})) return HSTU_ERR_INVALID_ARG;
+  if (batch > 0 && total_tokens > 0) {
+    if (any_null({seq_offsets, q, k, v, u, ts, dy, grads->dq, grads->dk, grads->dv, grads->du}))
+      return HSTU_ERR_INVALID_ARG;
+    if (any_misaligned({q, k, v, u, ts, dy, grads->dq, grads->dk, grads->dv, grads->du}))
+      return HSTU_ERR_INVALID_ARG;
+  }
+  WsLayout w;
+  if (!layout(HSTU_FN_FULL_BWD, params, batch, total_tokens, max_len, w)) return HSTU_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < w.total || !aligned16(ws)) return HSTU_ERR_WORKSPACE;
+  const bool empty = batch == 0 || total_tokens == 0;
+  auto mark = [&](int i) {
+    hipEvent_t ev = (hipEvent_t)params->timing_events[i];
+    return !ev || hipEventRecord(ev, stream) == hipSuccess;
+  };
+  const int HD = params->num_heads * params->head_dim;
+
+  // 1. recompute the attention output O (fp32, in the workspace)
+  SchedArgs s = sched_args(MODE_FULL, params, w, ws, batch, seq_offsets, max_len);
+  s.ts = ts;
+  s.Tk = total_tokens;
+  AttnArgs a = base_args(params, w, ws, total_tokens);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.ts = ts;
+  a.offsets = seq_offsets;
+  if (!mark(0)) return HSTU_ERR_LAUNCH;
+  if (!empty) {
+    if (launch_sched(s, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+    if (launch_attn(a, params->dtype, params->head_dim, MODE_FULL, s.max_items, stream) != hipSuccess)
+      return HSTU_ERR_LAUNCH;
+  }
+  // 2. norm + gating backward: dU, dO, affine gradients
+  LnBwdArgs l = {};
+  l.o = (const float*)((char*)ws + w.o_off);
+  l.u = u;
+  l.dy = dy;
+  l.ln_w = params->ln_w;
+  l.ln_b = params->ln_b;
+  l.eps = params->ln_eps;
+  l.HD = HD;
+  l.T = empty ? 0 : total_tokens;
+  l.du = grads->du;
+  l.dout = (char*)ws + w.dout_off;
+  l.part = (params->ln_w || params->ln_b) ? (float*)((char*)ws + w.lnp_off) : nullptr;
+  l.nwaves = empty ? 0 : w.ln_waves;
+  l.d_ln_w = grads->d_ln_w;
+  l.d_ln_b = grads->d_ln_b;
+  if (!mark(1) || launch_ln_bwd(l, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  // 3. attention backward
+  BwdArgs g = {};
+  g.q = q;
+  g.k = k;
+  g.v = v;
+  g.dout = l.dout;
+  g.ts = ts;
+  g.offsets = seq_offsets;
+  g.pos_tab = params->pos_tab;
+  g.n_pos = params->n_pos;
+  g.pos_stride = params->pos_head_stride;
+  g.time_tab = params->time_tab;
+  g.n_time = params->n_time;
+  g.time_stride = params->time_head_stride;
+  g.alpha = params->alpha;
+  g.norm_n = params->norm_n;
+  g.H = params->num_heads;
+  g.T = total_tokens;
+  g.items = a.items;
+  g.count = a.count;
+  g.prefix = s.prefix;
+  g.tstats = a.tstats;
+  g.n_stat_blocks = a.n_stat_blocks;
+  g.dq = grads->dq;
+  g.dk = grads->dk;
+  g.dv = grads->dv;
+  g.rab_part = (float*)((char*)ws + w.rab_off);
+  if (!mark(2)) return HSTU_ERR_LAUNCH;
+  if (!empty && launch_attn_bwd(g, params->head_dim, s.max_items, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  // 4. bias-table gradients
+  RabReduceArgs r = {};
+  r.part = g.rab_part;
+  r.offsets = seq_offsets;
+  r.prefix = s.prefix;
+  r.B = empty ? 0 : batch;
+  r.H = params->num_heads;
+  r.d_pos = grads->d_pos_tab;
+  r.n_pos = params->n_pos;
+  r.pos_stride = params->pos_head_stride;
+  r.d_time = grads->d_time_tab;
+  r.n_time = params->n_time;
+  r.time_stride = params->time_head_stride;
+  if (launch_rab_reduce(r, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  if (!mark(3)) return HSTU_ERR_LAUNCH;
+  return HSTU_OK;
 }
 
 hstu_status_t hstu_mfalcon_fwd(const hstu_params_t* params, int32_t batch, const int32_t* seq_offsets,

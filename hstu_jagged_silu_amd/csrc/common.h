@@ -51,6 +51,9 @@ struct WsLayout {
   int64_t max_items;
   int32_t n_chunks;       // key splits (1 except on the cached path)
   int32_t chunk_keys;     // keys per split (multiple of KT)
+  // backward only: dO (bf16), bias-table gradient partials, affine partials
+  size_t dout_off, rab_off, lnp_off;
+  int32_t ln_waves;
 };
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -97,9 +97,75 @@ struct AppendArgs {
   int64_t T;
 };
 
+// Backward of the full causal path (bf16). The bias-table gradients of each
+// work item go to rab_part[canonical item][RAB_SLOTS] (position buckets at
+// [0, n_pos), time buckets at [BWD_MAX_NPOS, BWD_MAX_NPOS + 64)) and are
+// summed in a fixed order by the reduce kernel, so results are reproducible.
+constexpr int BWD_MAX_NPOS = 512;
+constexpr int RAB_SLOTS = BWD_MAX_NPOS + 64;
+
+struct BwdArgs {
+  const void* q;                 // [T, H, D]
+  const void* k;
+  const void* v;
+  const void* dout;              // [T, H, D] bf16: gradient reaching the attention output
+  const int64_t* ts;             // [T]
+  const int32_t* offsets;        // [B+1]
+  const float* pos_tab;
+  int32_t n_pos, pos_stride;
+  const float* time_tab;
+  int32_t n_time, time_stride;
+  float alpha;
+  int32_t norm_n;
+  int32_t H;
+  int64_t T;
+  const WorkItem* items;         // scheduler output of the full path
+  const int32_t* count;
+  const int32_t* prefix;         // [B+1] first canonical item of each user
+  const int64_t* tstats;         // key timestamp ranges per packed 64-row block
+  int64_t n_stat_blocks;
+  void* dq;                      // [T, H, D] bf16
+  void* dk;
+  void* dv;
+  float* rab_part;               // [items][RAB_SLOTS]
+};
+
+struct RabReduceArgs {
+  const float* part;
+  const int32_t* offsets;
+  const int32_t* prefix;
+  int32_t B, H;
+  float* d_pos;                  // like pos_tab: [n_pos] shared or [H][pos_stride]
+  int32_t n_pos, pos_stride;
+  float* d_time;
+  int32_t n_time, time_stride;
+};
+
+// LayerNorm + U gating backward: per row dU and the gradient reaching O
+// (bf16), plus per-wave partial sums of the affine gradients.
+struct LnBwdArgs {
+  const float* o;                // [T, HD] attention output before the norm
+  const void* u;
+  const void* dy;
+  const float* ln_w;
+  const float* ln_b;
+  float eps;
+  int32_t HD;
+  int64_t T;
+  void* du;                      // [T, HD], dtype of u
+  void* dout;                    // [T, HD] bf16
+  float* part;                   // [2][nwaves][HD] (dw, db), or null
+  int32_t nwaves;
+  float* d_ln_w;
+  float* d_ln_b;
+};
+
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s);  // scheduler + key timestamp ranges
 hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int mode, int64_t grid, hipStream_t s);
 hipError_t launch_ln_gate(const LnArgs& a, int dtype, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_ln_bwd(const LnBwdArgs& a, hipStream_t s);       // rows, then the affine reduce
+hipError_t launch_attn_bwd(const BwdArgs& a, int D, int64_t grid, hipStream_t s);
+hipError_t launch_rab_reduce(const RabReduceArgs& a, hipStream_t s);
 
 }  // namespace hstu

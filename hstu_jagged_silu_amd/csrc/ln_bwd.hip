@@ -1,0 +1,170 @@
+// Backward of the LayerNorm + U gating epilogue, y = (n * w + b) * u with
+// n = (o - mean) * rstd over the H*d values of a token (population variance).
+// The chain rule of that definition gives, per row,
+//   du = dy * (n * w + b),   g = dy * u * w,
+//   do = rstd * (g - mean(g) - n * mean(g * n)),
+// and over all rows dw = sum dy * u * n, db = sum dy * u. The norm and gating
+// follow "How Generative Recommenders Are Redefining RecSys at Scale",
+// Takeaways (elementwise gating before the output projection).
+//
+// One wave64 per row at a time; each wave walks rows with a grid-wide stride
+// and keeps its share of dw and db in registers, written once as a per-wave
+// partial. A second kernel adds the partials in wave order (reproducible).
+// HBM-bound: per element it reads O (4 B), U and dY (2 B each) and writes dU
+// and dO (2 B each).
+#include "kernels.h"
+
+namespace hstu {
+
+constexpr int LNB_WAVES = 4;  // waves per workgroup
+
+__device__ inline float lnb_wave_sum(float x) {
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+__device__ inline f32x4 ld_bf4(const bf16* p) {
+  const bf16x4 v = *(const bf16x4*)p;
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+__device__ inline void st_bf4(bf16* p, f32x4 x) {
+  bf16x4 v;
+  for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
+  *(bf16x4*)p = v;
+}
+
+// NCH: 4-element chunks per lane (see ln_gate_kernel)
+template <int NCH, bool FULL_LANES>
+__global__ __launch_bounds__(64 * LNB_WAVES) void ln_bwd_kernel(LnBwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * LNB_WAVES + (threadIdx.x >> 6);
+  if (wave >= a.nwaves) return;
+  const int nch = a.HD / 4;
+  bool on[NCH];
+  int col[NCH];
+  f32x4 w[NCH], bb[NCH], dw[NCH], db[NCH];
+  #pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    on[i] = FULL_LANES || c < nch;
+    col[i] = 4 * (FULL_LANES ? c : min(c, nch - 1));
+    w[i] = a.ln_w ? *(const f32x4*)(a.ln_w + col[i]) : f32x4{1, 1, 1, 1};
+    bb[i] = a.ln_b ? *(const f32x4*)(a.ln_b + col[i]) : f32x4{0, 0, 0, 0};
+    dw[i] = f32x4{0, 0, 0, 0};
+    db[i] = f32x4{0, 0, 0, 0};
+  }
+  const float inv_hd = 1.0f / (float)a.HD;
+  for (int64_t row = wave; row < a.T; row += a.nwaves) {
+    const float* orow = a.o + row * a.HD;
+    const bf16* urow = (const bf16*)a.u + row * a.HD;
+    const bf16* yrow = (const bf16*)a.dy + row * a.HD;
+    f32x4 z[NCH], u[NCH], g[NCH];
+    #pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      z[i] = *(const f32x4*)(orow + col[i]);
+      u[i] = ld_bf4(urow + col[i]);
+      g[i] = ld_bf4(yrow + col[i]);  // dy for now
+    }
+    float s = 0.0f;
+    #pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      if (on[i]) s += (z[i][0] + z[i][1]) + (z[i][2] + z[i][3]);
+    const float mean = lnb_wave_sum(s) * inv_hd;
+    float ss = 0.0f;
+    #pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      if (!on[i]) continue;
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z[i][e] -= mean;
+        ss = fmaf(z[i][e], z[i][e], ss);
+      }
+    }
+    const float rstd = rsqrtf(lnb_wave_sum(ss) * inv_hd + a.eps);
+    bf16* durow = (bf16*)a.du + row * a.HD;
+    float s1 = 0.0f, s2 = 0.0f;
+    #pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      f32x4 du;
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float n = z[i][e] * rstd;
+        z[i][e] = n;
+        du[e] = g[i][e] * fmaf(n, w[i][e], bb[i][e]);
+        const float gu = g[i][e] * u[i][e];  // gradient reaching n * w + b
+        dw[i][e] = fmaf(gu, n, dw[i][e]);
+        db[i][e] += gu;
+        g[i][e] = gu * w[i][e];              // gradient reaching n
+      }
+      if (on[i]) {
+        st_bf4(durow + col[i], du);
+        s1 += (g[i][0] + g[i][1]) + (g[i][2] + g[i][3]);
+        #pragma unroll
+        for (int e = 0; e < 4; ++e) s2 = fmaf(g[i][e], z[i][e], s2);
+      }
+    }
+    const float m1 = lnb_wave_sum(s1) * inv_hd, m2 = lnb_wave_sum(s2) * inv_hd;
+    bf16* dorow = (bf16*)a.dout + row * a.HD;
+    #pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      if (!on[i]) continue;
+      f32x4 d;
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) d[e] = rstd * (g[i][e] - m1 - z[i][e] * m2);
+      st_bf4(dorow + col[i], d);
+    }
+  }
+  if (a.part) {
+    float* pw = a.part + (int64_t)wave * a.HD;
+    float* pb = a.part + ((int64_t)a.nwaves + wave) * a.HD;
+    #pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      if (!on[i]) continue;
+      *(f32x4*)(pw + col[i]) = dw[i];
+      *(f32x4*)(pb + col[i]) = db[i];
+    }
+  }
+}
+
+// dw[c] = sum over waves of the partials, in wave order
+__global__ __launch_bounds__(256) void ln_affine_reduce_kernel(LnBwdArgs a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.HD) return;
+  float sw = 0.0f, sb = 0.0f;
+  for (int w = 0; a.part && w < a.nwaves; ++w) {
+    sw += a.part[(int64_t)w * a.HD + c];
+    sb += a.part[((int64_t)a.nwaves + w) * a.HD + c];
+  }
+  if (a.d_ln_w) a.d_ln_w[c] = sw;
+  if (a.d_ln_b) a.d_ln_b[c] = sb;
+}
+
+hipError_t launch_ln_bwd(const LnBwdArgs& a, hipStream_t s) {
+  if (a.HD <= 0) return hipSuccess;
+  if (a.T <= 0 || a.nwaves <= 0) {  // no rows: the affine gradients are zero
+    if (!a.d_ln_w && !a.d_ln_b) return hipSuccess;
+    hipLaunchKernelGGL(ln_affine_reduce_kernel, dim3((unsigned)ceil_div(a.HD, 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)ceil_div(a.nwaves, LNB_WAVES)), blk(64 * LNB_WAVES);
+  switch (a.HD) {
+    case 256: hipLaunchKernelGGL((ln_bwd_kernel<1, true>), grid, blk, 0, s, a); break;
+    case 512: hipLaunchKernelGGL((ln_bwd_kernel<2, true>), grid, blk, 0, s, a); break;
+    case 1024: hipLaunchKernelGGL((ln_bwd_kernel<4, true>), grid, blk, 0, s, a); break;
+    case 2048: hipLaunchKernelGGL((ln_bwd_kernel<8, true>), grid, blk, 0, s, a); break;
+    default: {
+      const int nch = (int)ceil_div(a.HD / 4, 64);
+      if (nch <= 1) hipLaunchKernelGGL((ln_bwd_kernel<1, false>), grid, blk, 0, s, a);
+      else if (nch <= 2) hipLaunchKernelGGL((ln_bwd_kernel<2, false>), grid, blk, 0, s, a);
+      else if (nch <= 4) hipLaunchKernelGGL((ln_bwd_kernel<4, false>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((ln_bwd_kernel<8, false>), grid, blk, 0, s, a);
+    }
+  }
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  if (a.d_ln_w || a.d_ln_b)
+    hipLaunchKernelGGL(ln_affine_reduce_kernel, dim3((unsigned)ceil_div(a.HD, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hstu

@@ -75,7 +75,8 @@ typedef enum {
   HSTU_FN_FULL = 0,
   HSTU_FN_CACHED = 1,
   HSTU_FN_MFALCON = 2,
-  HSTU_FN_MFALCON_CACHED = 3
+  HSTU_FN_MFALCON_CACHED = 3,
+  HSTU_FN_FULL_BWD = 4
 } hstu_fn_t;
 
 /*
@@ -173,6 +174,51 @@ hstu_status_t hstu_attn_fwd(const hstu_params_t* params, int32_t batch, const in
                             int32_t max_len, int64_t total_tokens, const void* q, const void* k,
                             const void* v, const void* u, const int64_t* ts, void* y, void* ws,
                             size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Gradients written by hstu_attn_bwd. dq, dk, dv: [T, H, d]; du: [T, H*d];
+ * all bf16. d_pos_tab and d_time_tab are fp32 with the layout of
+ * params->pos_tab / time_tab ([n] when the head stride is 0, else [H][stride];
+ * entries past n_pos / n_time in a row are left untouched); each may be NULL
+ * to skip that gradient and must be NULL when its table is. d_ln_w, d_ln_b:
+ * fp32 [H*d], NULL to skip, NULL when the matching affine term is. Every
+ * requested gradient is overwritten, not accumulated.
+ */
+typedef struct {
+  void* dq;
+  void* dk;
+  void* dv;
+  void* du;
+  float* d_pos_tab;
+  float* d_time_tab;
+  float* d_ln_w;
+  float* d_ln_b;
+} hstu_grads_t;
+
+/*
+ * Backward of hstu_attn_fwd (training). Given the forward's inputs and dy,
+ * the gradient of the loss with respect to y, writes the gradients of q, k,
+ * v, u, the bias tables and the norm's affine terms. The pages print no
+ * backward; it is the chain rule of the forward (pointwise SiLU attention
+ * with relative bias, "Generative recommenders at scale", section "Inside
+ * NVIDIA's GPU-native stack for HSTU and Semantic IDs"; norm and gating, "How
+ * Generative Recommenders Are Redefining RecSys at Scale", Takeaways), for
+ * the training workload of "HSTU Generative Recommenders: Deploy on GPU
+ * Cloud", section "Scaling Training and Serving Across Multiple GPUs".
+ * The attention output is recomputed inside the call (nothing is saved
+ * between forward and backward).
+ *   arguments as hstu_attn_fwd, plus dy [T, H*d] and grads (see above)
+ *   ws, ws_bytes  workspace of at least hstu_workspace_size(HSTU_FN_FULL_BWD, ...)
+ * bf16 only (HSTU_ERR_UNSUPPORTED for fp32) and n_pos <= 512. Outputs must
+ * not alias inputs. All tensors 16-byte aligned. Results do not depend on
+ * scheduling: every sum runs in a fixed order. params->timing_events, if
+ * set, are recorded [0] before the recomputed forward, [1] before the norm
+ * backward, [2] before the attention backward, [3] at the end.
+ */
+hstu_status_t hstu_attn_bwd(const hstu_params_t* params, int32_t batch, const int32_t* seq_offsets,
+                            int32_t max_len, int64_t total_tokens, const void* q, const void* k,
+                            const void* v, const void* u, const int64_t* ts, const void* dy,
+                            const hstu_grads_t* grads, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Paged KV append: new token m of user b (packed row new_offsets[b] + m)

@@ -60,7 +60,7 @@ __all__ = [
     "time_bucket", "pos_bucket", "silu", "layer_norm_gate",
     "hstu_full", "hstu_full_rows", "hstu_cached", "hstu_mfalcon",
     "kv_append_pages", "hstu_layer", "max_rel_row_error", "pair_count",
-    "silu_grad", "layer_norm_gate_bwd", "hstu_full_bwd",
+    "silu_grad", "layer_norm_gate_bwd", "hstu_full_bwd", "max_rel_err_vs_magnitude",
 ]
 
 
@@ -424,7 +424,7 @@ def layer_norm_gate_bwd(z, u, dy, gamma=None, beta=None, eps=1e-5):
 
 
 def hstu_full_bwd(q, k, v, u, ts, seq_offsets, dy, pos_tab=None, time_tab=None, alpha=1.0, norm_n=0,
-                  gamma=None, beta=None, eps=1e-5):
+                  gamma=None, beta=None, eps=1e-5, magnitudes=False):
     """Gradients of the full causal path (hstu_full) for an upstream gradient dy [T, H*d].
 
     Per sequence and head, with s = alpha q k^T + bias, a = SiLU(s) / N on
@@ -438,6 +438,12 @@ def hstu_full_bwd(q, k, v, u, ts, seq_offsets, dy, pos_tab=None, time_tab=None, 
     The norm and gating gradients come from layer_norm_gate_bwd.
     Returns a dict with dq, dk, dv ([T, H, d]), du ([T, H*d]), dpos, dtime
     (shaped like the tables, None without one), dgamma, dbeta.
+
+    With magnitudes=True the dict also holds, under "mag_<name>", the same
+    sums taken over absolute values (|do| |v|^T for da, |da| |SiLU'| / N for
+    ds, and so on): the scale against which rounding errors of the summed
+    terms are measured (a gradient that is small only by cancellation has a
+    large magnitude).
     """
     H, d = _heads(q)
     T = q.shape[0]
@@ -450,6 +456,19 @@ def hstu_full_bwd(q, k, v, u, ts, seq_offsets, dy, pos_tab=None, time_tab=None, 
     dv = np.zeros((T, H, d))
     dpos = None if pos_tab is None else np.zeros(np.shape(pos_tab))
     dtime = None if time_tab is None else np.zeros(np.shape(time_tab))
+    mag = {}
+    if magnitudes:
+        mag = {"mag_dq": np.zeros((T, H, d)), "mag_dk": np.zeros((T, H, d)), "mag_dv": np.zeros((T, H, d)),
+               "mag_du": np.abs(du),
+               "mag_dpos": None if dpos is None else np.zeros_like(dpos),
+               "mag_dtime": None if dtime is None else np.zeros_like(dtime)}
+        if dgamma is not None or dbeta is not None:
+            z = np.asarray(o, dtype=np.float64)
+            mu = z.mean(axis=-1, keepdims=True)
+            nrm = (z - mu) / np.sqrt(((z - mu) ** 2).mean(axis=-1, keepdims=True) + eps)
+            gu = np.abs(np.asarray(dy, dtype=np.float64) * np.asarray(u, dtype=np.float64))
+            mag["mag_dgamma"] = None if dgamma is None else (gu * np.abs(nrm)).sum(axis=0)
+            mag["mag_dbeta"] = None if dbeta is None else gu.sum(axis=0)
     for b in range(len(off) - 1):
         s0, s1 = int(off[b]), int(off[b + 1])
         L = s1 - s0
@@ -479,8 +498,19 @@ def hstu_full_bwd(q, k, v, u, ts, seq_offsets, dy, pos_tab=None, time_tab=None, 
             if dtime is not None:
                 row = dtime if dtime.ndim == 1 else dtime[h]
                 np.add.at(row, time_bucket(dt[allowed], row.shape[0]), ds[allowed])
-    return {"dq": dq, "dk": dk, "dv": dv, "du": du, "dpos": dpos, "dtime": dtime,
-            "dgamma": dgamma, "dbeta": dbeta}
+            if magnitudes:
+                ds_m = np.where(allowed, (np.abs(doh) @ np.abs(vh).T) * np.abs(silu_grad(s)), 0.0) / float(n_norm)
+                mag["mag_dq"][s0:s1, h] = abs(alpha) * (ds_m @ np.abs(kh))
+                mag["mag_dk"][s0:s1, h] = abs(alpha) * (ds_m.T @ np.abs(qh))
+                mag["mag_dv"][s0:s1, h] = np.abs(a).T @ np.abs(doh)
+                for key, rel_or_dt, fn in (("mag_dpos", rel, pos_bucket), ("mag_dtime", dt, time_bucket)):
+                    if mag[key] is not None:
+                        row = mag[key] if mag[key].ndim == 1 else mag[key][h]
+                        np.add.at(row, fn(rel_or_dt[allowed], row.shape[0]), ds_m[allowed])
+    out = {"dq": dq, "dk": dk, "dv": dv, "du": du, "dpos": dpos, "dtime": dtime,
+           "dgamma": dgamma, "dbeta": dbeta}
+    out.update(mag)
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -505,6 +535,27 @@ def max_rel_row_error(y, y_ref, zero_row_atol=1e-6):
     if np.any(zero & (np.abs(y).max(axis=1) > zero_row_atol)):
         return float("inf")
     return float(err.max())
+
+
+def max_rel_err_vs_magnitude(g, g_ref, mag):
+    """max over rows t of ||g_t - g*_t||_inf / ||mag_t||_inf.
+
+    mag is the same sum as g* over absolute values of the terms, so this is
+    the error relative to the size of what was added up; it stays meaningful
+    for a row whose gradient is small through cancellation. A 1-D input is
+    one row. Rows whose magnitude is zero must match exactly (else inf).
+    """
+    g = np.asarray(g, dtype=np.float64)
+    g_ref = np.asarray(g_ref, dtype=np.float64)
+    mag = np.asarray(mag, dtype=np.float64)
+    n = len(g_ref) if g_ref.ndim > 1 else 1
+    g, g_ref, mag = (x.reshape(n, -1) for x in (g, g_ref, mag))
+    num = np.abs(g - g_ref).max(axis=1)
+    den = mag.max(axis=1)
+    zero = den == 0
+    if np.any(zero & (num > 0)):
+        return float("inf")
+    return float(np.where(zero, 0.0, num / np.where(zero, 1.0, den)).max()) if n else 0.0
 
 
 def pair_count(kind, lengths, extra=None):

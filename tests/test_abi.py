@@ -56,6 +56,9 @@ int main(void) {
   P(hstu_kv_cache_t, k_pages); P(hstu_kv_cache_t, v_pages); P(hstu_kv_cache_t, ts_pages);
   P(hstu_kv_cache_t, page_table); P(hstu_kv_cache_t, num_pages); P(hstu_kv_cache_t, page_size);
   P(hstu_kv_cache_t, max_pages_per_seq);
+  printf("hstu_grads_t %zu\n", sizeof(hstu_grads_t));
+  P(hstu_grads_t, dq); P(hstu_grads_t, dk); P(hstu_grads_t, dv); P(hstu_grads_t, du);
+  P(hstu_grads_t, d_pos_tab); P(hstu_grads_t, d_time_tab); P(hstu_grads_t, d_ln_w); P(hstu_grads_t, d_ln_b);
   printf("hstu_layer_weights_t %zu\n", sizeof(hstu_layer_weights_t));
   P(hstu_layer_weights_t, embed_dim); P(hstu_layer_weights_t, w1); P(hstu_layer_weights_t, w2);
   return 0;
@@ -73,6 +76,9 @@ int main(void) {
         assert int(got[f"hstu_params_t.{name}"]) == getattr(hs._Params, name).offset, name
     for name, _ in hs._KVCache._fields_:
         assert int(got[f"hstu_kv_cache_t.{name}"]) == getattr(hs._KVCache, name).offset, name
+    assert int(got["hstu_grads_t"]) == ctypes.sizeof(hs._Grads)
+    for name, _ in hs._Grads._fields_:
+        assert int(got[f"hstu_grads_t.{name}"]) == getattr(hs._Grads, name).offset, name
     assert int(got["hstu_layer_weights_t"]) == ctypes.sizeof(hs._LayerWeights)
     for name, _ in hs._LayerWeights._fields_:
         assert int(got[f"hstu_layer_weights_t.{name}"]) == getattr(hs._LayerWeights, name).offset, name
@@ -226,6 +232,33 @@ def test_paged_mfalcon_rejects_bad_arguments_before_launch():
     assert call(T=0) == OK
     c.page_size = 32
     assert call(wsb=1 << 40) == UNSUPPORTED
+
+
+def test_backward_workspace_and_bad_arguments_before_launch():
+    lib = hs.lib()
+    p = _params()
+    fwd, bwd = _ws(0, p, 8, 8192, 1024), _ws(4, p, 8, 8192, 1024)
+    assert bwd >= fwd + 8192 * 512 * 2                   # plus the bf16 gradient reaching O
+    tab = _params(pos_tab=FAKE, n_pos=128, ln_w=FAKE)
+    assert _ws(4, tab, 8, 8192, 1024) > bwd               # table and affine partials
+    f = lib.hstu_attn_bwd
+
+    def call(p=p, g=None, B=2, T=32, q=FAKE, wsb=0, grads=True):
+        if g is None:
+            g = hs._Grads(FAKE, FAKE, FAKE, FAKE, None, None, None, None)
+        return f(ctypes.byref(p), B, FAKE, 16, T, q, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 ctypes.byref(g) if grads else None, FAKE, wsb, None)
+
+    assert call() == WORKSPACE
+    assert call(p=_params(dtype=0)) == UNSUPPORTED                            # fp32
+    assert call(p=_params(pos_tab=FAKE, n_pos=513)) == UNSUPPORTED            # position table too long
+    assert call(grads=False, wsb=1 << 40) == INVALID
+    assert call(g=hs._Grads(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None), wsb=1 << 40) == INVALID  # no table
+    assert call(g=hs._Grads(FAKE, FAKE, FAKE, None, None, None, None, None), wsb=1 << 40) == INVALID  # no du
+    assert call(q=None, wsb=1 << 40) == INVALID
+    assert call(q=FAKE + 4, wsb=1 << 40) == INVALID
+    assert call(p=_params(head_dim=48)) == UNSUPPORTED
+    assert call(B=0, wsb=1 << 40) == OK      # nothing to compute and no table or affine gradient requested
 
 
 def test_pair_count_matches_closed_forms():

@@ -95,3 +95,28 @@ def test_silu_grad_closed_forms():
     sg = 1 / (1 + np.exp(-x))
     np.testing.assert_allclose(oracle.silu_grad(x), sg + x * sg * (1 - sg), rtol=1e-15)
     assert abs(oracle.silu_grad(60.0) - 1.0) < 1e-20 + 1e-15
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_magnitudes_bound_the_gradients(case):
+    """Each magnitude is the same sum over absolute values, so it bounds |g| (triangle inequality)."""
+    lengths, H, d, n_pos, n_time, php, pht, aff, alpha, norm_n = CASES[case]
+    x, ts, off, dy = _case(50 + case, lengths, H, d, n_pos, n_time, php, pht, aff)
+    g = oracle.hstu_full_bwd(x["q"], x["k"], x["v"], x["u"], ts, off, dy, x["pos_tab"], x["time_tab"], alpha,
+                             norm_n, x["gamma"], x["beta"], magnitudes=True)
+    for name in ("dq", "dk", "dv", "du", "dpos", "dtime", "dgamma", "dbeta"):
+        if g[name] is None:
+            continue
+        assert np.all(g["mag_" + name] >= np.abs(g[name]) * (1 - 1e-12)), name
+    assert oracle.max_rel_err_vs_magnitude(g["dq"].reshape(len(g["dq"]), -1), g["dq"].reshape(len(g["dq"]), -1),
+                                           g["mag_dq"].reshape(len(g["dq"]), -1)) == 0.0
+
+
+def test_magnitude_equals_value_without_cancellation():
+    """One token, one head: dv = a dO has a single term, so |dv| equals its magnitude."""
+    x, ts, off, dy = _case(9, [1], 1, 4, 4, 6, False, False, True)
+    g = oracle.hstu_full_bwd(x["q"], x["k"], x["v"], x["u"], ts, off, dy, x["pos_tab"], x["time_tab"],
+                             magnitudes=True)
+    np.testing.assert_allclose(g["mag_dv"], np.abs(g["dv"]), rtol=1e-14)
+    # dq's terms carry the sum over d inside da = dO . v, so there it only bounds
+    assert np.all(g["mag_dq"] >= np.abs(g["dq"]))

@@ -339,3 +339,16 @@ def full_layer(seed: int = 5, batch: int = 16, embed: int = 1024, num_heads: int
     tables = _tables(rng, 128, 128)
     return LayerInputs(f"layer_B{batch}_D{embed}_H{num_heads}_d{head_dim}_bf16", lengths,
                        offsets_from_lengths(lengths), ts, x, w1, w2, num_heads, head_dim, tables)
+
+
+def upstream_grad(seed: int, shape, dtype: str = "bf16") -> np.ndarray:
+    """Gradient of a training loss with respect to the layer output, N(0, 1) (seeded)."""
+    return _normal(np.random.default_rng(seed), tuple(shape), dtype)
+
+
+def affine_terms(seed: int, width: int):
+    """LayerNorm affine terms: weight ~ N(1, 0.1^2), bias ~ N(0, 0.1^2), fp32."""
+    rng = np.random.default_rng(seed)
+    w = (1.0 + 0.1 * rng.standard_normal(width, dtype=np.float32)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(width, dtype=np.float32)).astype(np.float32)
+    return w, b
