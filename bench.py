@@ -263,6 +263,45 @@ def bench_training_shape(torch, hs, W, steps, warmup):
     }
 
 
+def _bench_backward(torch, hs, W, inp, steps, warmup):
+    """hstu_attn_bwd: recomputed forward, norm backward, attention backward."""
+    bf = torch.bfloat16
+    H, d = inp.num_heads, inp.head_dim
+    q, k, v, u = (dev(torch, x, bf) for x in (inp.q, inp.k, inp.v, inp.u))
+    ts, off = dev(torch, inp.ts), dev(torch, inp.seq_offsets)
+    dy = dev(torch, W.upstream_grad(81, inp.u.shape), bf)
+    w, b = W.affine_terms(82, H * d)
+    p = hs.LayerParams(num_heads=H, head_dim=d, dtype=bf, pos_tab=dev(torch, inp.tables.pos),
+                       time_tab=dev(torch, inp.tables.time), ln_w=dev(torch, w), ln_b=dev(torch, b))
+    ws = torch.empty(hs.hstu_workspace_size(hs.HSTU_FN_FULL_BWD, p, inp.batch, inp.total, inp.max_len),
+                     dtype=torch.uint8, device="cuda")
+    fn = lambda ev: hs.hstu_attn_bwd(q, k, v, u, ts, off, inp.max_len, dy, p, workspace=ws, timing_events=ev)
+    ms, evs = timed(fn, steps, warmup, torch)
+    pairs = H * hs.pair_count("full", [int(x) for x in inp.lengths])
+    bwd_flop = 5 * 2 * d * pairs      # S recomputed, dP, dV, dQ, dK: five products of 2*d FLOP per pair
+    fwd_ms, ln_ms, attn_ms = mean_span(evs, 0, 1), mean_span(evs, 1, 2), mean_span(evs, 2, 3)
+    return {
+        "workload": inp.name,
+        "total_tokens": inp.total,
+        "ms_per_step": round(ms, 4),
+        "forward_recompute_ms": round(fwd_ms, 4),
+        "norm_backward_ms": round(ln_ms, 4),
+        "attention_backward_ms": round(attn_ms, 4),
+        "attention_backward_tflops": round(bwd_flop / (attn_ms * 1e-3) / 1e12, 2),
+        "attention_backward_pct_bf16_peak": round(100 * bwd_flop / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "algorithmic_gflop": round(bwd_flop / 1e9, 3),
+        "norm_backward_gbs": round(inp.total * H * d * (4 + 2 + 2 + 2 + 2) / (ln_ms * 1e-3) / 1e9, 1),
+    }
+
+
+def bench_backward_training(torch, hs, W, steps, warmup):
+    return _bench_backward(torch, hs, W, W.training_shape(), steps, warmup)
+
+
+def bench_backward_long(torch, hs, W, steps, warmup):
+    return _bench_backward(torch, hs, W, W.long_seq(), steps, warmup)
+
+
 def bench_layer(torch, hs, W, steps, warmup):
     """Full layer: f1 + SiLU (4 hipBLASLt products), attention, f2."""
     inp = W.full_layer()
@@ -411,7 +450,9 @@ def main():
         variants = {}
         for name, fn in (("kv_cache_delta", bench_cached), ("mfalcon", bench_mfalcon),
                          ("mfalcon_paged_history", bench_mfalcon_paged),
-                         ("jagged_training_shape", bench_training_shape), ("full_layer", bench_layer)):
+                         ("jagged_training_shape", bench_training_shape), ("full_layer", bench_layer),
+                         ("backward_training_shape", bench_backward_training),
+                         ("backward_causal_B8_L8192", bench_backward_long)):
             log(f"variant {name}")
             variants[name] = fn(torch, hs, W, args.steps, args.warmup)
             log(f"  {variants[name]}")

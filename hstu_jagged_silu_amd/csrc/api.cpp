@@ -319,6 +319,7 @@ hstu_status_t hstu_attn_bwd(const hstu_params_t* params, int32_t batch, const in
   g.items = a.items;
   g.count = a.count;
   g.prefix = s.prefix;
+  g.B = batch;
   g.tstats = a.tstats;
   g.n_stat_blocks = a.n_stat_blocks;
   g.dq = grads->dq;
@@ -330,7 +331,6 @@ hstu_status_t hstu_attn_bwd(const hstu_params_t* params, int32_t batch, const in
   // 4. bias-table gradients
   RabReduceArgs r = {};
   r.part = g.rab_part;
-  r.offsets = seq_offsets;
   r.prefix = s.prefix;
   r.B = empty ? 0 : batch;
   r.H = params->num_heads;

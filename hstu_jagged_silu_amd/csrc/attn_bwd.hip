@@ -56,16 +56,31 @@ __device__ inline float wave_sum_f(float x) {
   return x;
 }
 
-// Offset of this lane's transposing read (ds_read_b64_tr_b16) inside a tile
-// staged with the K swizzle: rows 16c .. 16c + 15 of the tile (c = 16-row
-// chunk), columns 32db .. 32db + 31, half s4 of the 8 rows a lane supplies.
+// XOR swizzle (on 16-byte chunks) of the tiles the backward reads both by
+// rows (16 lanes, 16 rows, one chunk) and transposed (32 lanes: 4 rows x 4
+// chunks per 256-byte window). For d = 128, s(r) = (r mod 16) xor 4 (r mod 4)
+// gives 16 rows 16 distinct chunk offsets, and 4 consecutive rows x 4 chunks
+// 16 distinct chunks, so both reads are free of bank conflicts. It depends on
+// r mod 16 only, so row offsets that are multiples of 16 can be added later.
+// Other head dims use the row swizzle of the forward.
 template <int D>
-__device__ inline uint32_t tr_off_k(int lane, int db, int c, int s4) {
+__device__ inline int swz_b(int r) {
+  if constexpr (D == 128) return (r & 15) ^ (4 * (r & 3));
+  else return Geo<bf16, D>::swz_k(r);
+}
+template <int D>
+__device__ inline int b_off(int r, int c) { return r * Geo<bf16, D>::ROWB + ((c ^ swz_b<D>(r)) << 4); }
+
+// Offset of this lane's transposing read (ds_read_b64_tr_b16): rows
+// 16c .. 16c + 15 of the tile (c = 16-row chunk), columns 32db .. 32db + 31,
+// half s4 of the 8 rows a lane supplies.
+template <int D>
+__device__ inline uint32_t tr_off_b(int lane, int db, int c, int s4) {
   using G = Geo<bf16, D>;
   const int tr_g = lane >> 4, tr_j = lane & 15;
   const int row = 16 * c + 8 * (tr_g >> 1) + 4 * s4 + (tr_j >> 2);
   const int d = 32 * db + 16 * (tr_g & 1) + 4 * (tr_j & 3);
-  return (uint32_t)(G::k_off(row, d / G::EPC) + (d % G::EPC) * 2);
+  return (uint32_t)(b_off<D>(row, d / G::EPC) + (d % G::EPC) * 2);
 }
 
 // y -> (P', dS') for one score: P' = y * sigma, dS' = dp * sigma * (1 + x (1 - sigma)), x = -ln2 y
@@ -93,7 +108,7 @@ __device__ inline void stage_rows(const BwdArgs& a, const void* x0, const void* 
     const int base = (wave * G::NDMA + i) * 64;
     const int P = base + lane;
     const int r = P / G::CPR, pc = P % G::CPR;
-    const int64_t off = min(r, last) * rstride + ((pc ^ G::swz_k(r)) << 4);
+    const int64_t off = min(r, last) * rstride + ((pc ^ swz_b<D>(r)) << 4);
     __builtin_amdgcn_global_load_lds((const void*)(b0 + off), LDS_PTR(void, st.k + base * 16), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)(b1 + off), LDS_PTR(void, st.v + base * 16), 16, 0, 0);
   }
@@ -151,7 +166,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   using T = bf16;
   using G = Geo<T, D>;
   using M = Mfma<T>;
-  __shared__ Stage<T, D> st0;  // k: K rows, v: V rows (both with the K swizzle)
+  __shared__ Stage<T, D> st0;  // k: K rows, v: V rows (both with swz_b)
   __shared__ Stage<T, D> st1;
   __shared__ BwdTables tab;
   __shared__ RabHist hist;
@@ -208,11 +223,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   {
     const int kr = M::krow(0, l32);
     #pragma unroll
-    for (int s = 0; s < G::NQOP; ++s) koff[s] = (uint32_t)G::k_off(kr, 2 * s + hl);
+    for (int s = 0; s < G::NQOP; ++s) koff[s] = (uint32_t)b_off<D>(kr, 2 * s + hl);
     #pragma unroll
     for (int db = 0; db < G::NDB; ++db) {
-      ktr[db][0] = tr_off_k<D>(lane, db, 0, 0);
-      ktr[db][1] = tr_off_k<D>(lane, db, 0, 1);
+      ktr[db][0] = tr_off_b<D>(lane, db, 0, 0);
+      ktr[db][1] = tr_off_b<D>(lane, db, 0, 1);
     }
   }
   f32x16 dqacc[G::NDB];
@@ -349,9 +364,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 
   store_rows_t<D>(dqacc, a.alpha / (float)n_norm, st0, st1, a.dq, q_off + q_start, q_len, h, H);
 
-  // per-item bias gradients (scaled by 1 / N), at the item's canonical index
-  const int nq = (int)ceil_div(L, QT);
-  const int64_t canon = (int64_t)ldc(a.prefix + b) + (int64_t)h * nq + q_start / QT;
+  // per-item bias gradients (scaled by 1 / N), head-major: the items of head h
+  // are [h * tiles, (h + 1) * tiles), tiles = query tiles over all users
+  // (the scheduler's prefix counts H items per tile)
+  const int64_t tiles = ldc(a.prefix + a.B) / H;
+  const int64_t canon = (int64_t)h * tiles + ldc(a.prefix + b) / H + q_start / QT;
   float* part = a.rab_part + canon * RAB_SLOTS;
   const float inv_n = 1.0f / (float)n_norm;
   if (a.pos_tab) {
@@ -378,7 +395,7 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
   using T = bf16;
   using G = Geo<T, D>;
   using M = Mfma<T>;
-  __shared__ Stage<T, D> st0;  // k: Q rows, v: dO rows (both with the K swizzle), ts64: query timestamps
+  __shared__ Stage<T, D> st0;  // k: Q rows, v: dO rows (both with swz_b), ts64: query timestamps
   __shared__ Stage<T, D> st1;
   __shared__ BwdTables tab;
 
@@ -406,7 +423,16 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
   const int64_t tsk = a.ts[krow];
   const int w_first = wave * 32;
   const bool w_keys = w_first < klen;
-  const int w_kmin = k0 + w_first;
+  const bool w_full = w_first + 31 < klen;          // every key of the wave valid
+  const int w_kmin = k0 + w_first, w_kmax = k0 + min(w_first + 31, klen - 1);
+  int64_t w_ts_min = key_ok ? tsk : INT64_MAX, w_ts_max = key_ok ? tsk : INT64_MIN;
+  for (int m = 32; m >= 1; m >>= 1) {
+    w_ts_min = min(w_ts_min, shfl_xor64(w_ts_min, m));
+    w_ts_max = max(w_ts_max, shfl_xor64(w_ts_max, m));
+  }
+  w_ts_min = uniform64(w_ts_min);
+  w_ts_max = uniform64(w_ts_max);
+  const int n_time_eff = a.time_tab ? min(a.n_time, 64) : 1;
 
   bf16x8 kop[G::NQOP], vop[G::NQOP];
   {
@@ -425,11 +451,11 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
   {
     const int qr = M::krow(0, l32);
     #pragma unroll
-    for (int s = 0; s < G::NQOP; ++s) qoff[s] = (uint32_t)G::k_off(qr, 2 * s + hl);
+    for (int s = 0; s < G::NQOP; ++s) qoff[s] = (uint32_t)b_off<D>(qr, 2 * s + hl);
     #pragma unroll
     for (int db = 0; db < G::NDB; ++db) {
-      qtr[db][0] = tr_off_k<D>(lane, db, 0, 0);
-      qtr[db][1] = tr_off_k<D>(lane, db, 0, 1);
+      qtr[db][0] = tr_off_b<D>(lane, db, 0, 0);
+      qtr[db][1] = tr_off_b<D>(lane, db, 0, 1);
     }
   }
   f32x16 dkacc[G::NDB], dvacc[G::NDB];
@@ -442,6 +468,26 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
   auto compute_tile = [&](Stage<T, D>& st, int j0) {
     // every query of the tile precedes every key of this wave: all masked
     if (!w_keys || j0 + KT - 1 < w_kmin) return;
+    // one bias constant and no mask for the whole wave tile? (as in the forward)
+    const bool need_mask = !w_full || j0 < w_kmax || j0 + KT > L;
+    const bool pos_uniform = (a.pos_tab == nullptr) || (j0 - w_kmax >= n_pos - 1);
+    bool time_uniform = !has_time;
+    int z_tile = 63;
+    if (has_time && !need_mask && pos_uniform) {
+      const int64_t r0 = q_off + j0;
+      const int64_t i0 = min(r0 / KT, a.n_stat_blocks - 1), i1 = min((r0 + KT - 1) / KT, a.n_stat_blocks - 1);
+      const int64_t q_min = min(ldc(a.tstats + 2 * i0), ldc(a.tstats + 2 * i1));
+      const int64_t q_max = max(ldc(a.tstats + 2 * i0 + 1), ldc(a.tstats + 2 * i1 + 1));
+      int64_t lo = -1, hi = -1;
+      if (q_min >= w_ts_max) { lo = q_min - w_ts_max; hi = q_max - w_ts_min; }
+      else if (w_ts_min >= q_max) { lo = w_ts_min - q_max; hi = w_ts_max - q_min; }
+      if (lo >= 0) {
+        const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
+        if (min(63 - zlo, n_time_eff - 1) == min(63 - zhi, n_time_eff - 1)) { time_uniform = true; z_tile = zlo; }
+      }
+    }
+    const bool fast = pos_uniform && time_uniform && !need_mask;
+    const float c_uni = (a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f) + (has_time ? tab.time_t[z_tile] : 0.0f);
     const int64_t* ts_l = st.ts64 + M::HLK * hl;
     LB* ql = LDS_PTR(unsigned char, st.k);
     LB* gl = LDS_PTR(unsigned char, st.v);
@@ -460,21 +506,31 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
         dp = M::run(ga, vop[i], dp);
       }
       bf16x8 pb[2], dsb[2];
-      #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int ql_ = M::key_of(qb, v, hl);  // query row within the tile
-        const int qpos = j0 + ql_;
-        const bool ok = key_ok && qpos >= kpos && qpos < L;
-        const int rel = qpos - kpos;
-        float cb = a.pos_tab ? tab.pos_t[min((unsigned)rel, (unsigned)(n_pos - 1))] : 0.0f;
-        if (has_time) {
-          const int64_t dt = ts_l[M::key_of(qb, v, 0)] - tsk;
-          cb += tab.time_t[__builtin_clzll((uint64_t)(dt < 0 ? -dt : dt) + 1u)];
+      if (fast) {
+        #pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float p, ds;
+          silu_fwd_bwd(fmaf(s[v], sc, c_uni), dp[v], p, ds);
+          pb[v >> 3][v & 7] = (bf16)p;
+          dsb[v >> 3][v & 7] = (bf16)ds;
         }
-        float p, ds;
-        silu_fwd_bwd(ok ? fmaf(s[v], sc, cb) : MASKED_Y, dp[v], p, ds);
-        pb[v >> 3][v & 7] = (bf16)p;
-        dsb[v >> 3][v & 7] = (bf16)ds;
+      } else {
+        #pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int ql_ = M::key_of(qb, v, hl);  // query row within the tile
+          const int qpos = j0 + ql_;
+          const bool ok = key_ok && qpos >= kpos && qpos < L;
+          const int rel = qpos - kpos;
+          float cb = a.pos_tab ? tab.pos_t[min((unsigned)rel, (unsigned)(n_pos - 1))] : 0.0f;
+          if (has_time) {
+            const int64_t dt = ts_l[M::key_of(qb, v, 0)] - tsk;
+            cb += tab.time_t[__builtin_clzll((uint64_t)(dt < 0 ? -dt : dt) + 1u)];
+          }
+          float p, ds;
+          silu_fwd_bwd(ok ? fmaf(s[v], sc, cb) : MASKED_Y, dp[v], p, ds);
+          pb[v >> 3][v & 7] = (bf16)p;
+          dsb[v >> 3][v & 7] = (bf16)ds;
+        }
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries of block qb
       #pragma unroll
@@ -519,32 +575,36 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
 // ============================================================================
 // Bias-table gradients: add the per-item histograms in canonical order
 // ============================================================================
-__global__ __launch_bounds__(256) void rab_reduce_kernel(RabReduceArgs a) {
-  // one thread per (head row, bucket) of the position table, then of the time table
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// Block (x, y): 64 buckets of table row y (a head, or the one shared row;
+// position rows first, then time rows). 16 groups of 64 threads split the
+// row's items (group g takes items g, g + 16, ...); one thread then adds the
+// 16 group sums in order, so the result does not depend on timing.
+constexpr int RAB_GROUPS = 16;
+__global__ __launch_bounds__(64 * RAB_GROUPS) void rab_reduce_kernel(RabReduceArgs a) {
+  __shared__ float acc[RAB_GROUPS][64];
+  const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int pos_rows = a.d_pos ? (a.pos_stride > 0 ? a.H : 1) : 0;
-  const int time_rows = a.d_time ? (a.time_stride > 0 ? a.H : 1) : 0;
-  const int64_t n_pos_out = (int64_t)pos_rows * a.n_pos;
-  const int64_t n_time_out = (int64_t)time_rows * a.n_time;
-  if (gid >= n_pos_out + n_time_out) return;
-  const bool is_pos = gid < n_pos_out;
-  const int64_t g = is_pos ? gid : gid - n_pos_out;
+  const int y = blockIdx.y;
+  const bool is_pos = y < pos_rows;
+  const int row = is_pos ? y : y - pos_rows;
   const int n = is_pos ? a.n_pos : a.n_time;
-  const int row = (int)(g / n), c = (int)(g % n);
+  const int c = blockIdx.x * 64 + cl;
   const bool shared = is_pos ? a.pos_stride == 0 : a.time_stride == 0;
+  const int64_t tiles = a.B > 0 ? a.prefix[a.B] / a.H : 0;
+  const int64_t lo = shared ? 0 : (int64_t)row * tiles, hi = shared ? (int64_t)a.H * tiles : lo + tiles;
   float sum = 0.0f;
-  if (is_pos || c < 64) {
+  if (c < n && (is_pos || c < 64)) {
     const int slot = is_pos ? c : BWD_MAX_NPOS + c;
-    for (int bb = 0; bb < a.B; ++bb) {
-      const int L = a.offsets[bb + 1] - a.offsets[bb];
-      const int nq = (int)ceil_div(L, QT);
-      for (int hh = shared ? 0 : row; hh < (shared ? a.H : row + 1); ++hh)
-        for (int t = 0; t < nq; ++t)
-          sum += a.part[((int64_t)a.prefix[bb] + (int64_t)hh * nq + t) * RAB_SLOTS + slot];
-    }
+    for (int64_t i = lo + grp; i < hi; i += RAB_GROUPS) sum += a.part[i * RAB_SLOTS + slot];
   }
-  if (is_pos) a.d_pos[(int64_t)row * a.pos_stride + c] = sum;
-  else a.d_time[(int64_t)row * a.time_stride + c] = sum;
+  acc[grp][cl] = sum;
+  __syncthreads();
+  if (grp == 0 && c < n) {
+    float t = 0.0f;
+    for (int g = 0; g < RAB_GROUPS; ++g) t += acc[g][cl];
+    if (is_pos) a.d_pos[(int64_t)row * a.pos_stride + c] = t;
+    else a.d_time[(int64_t)row * a.time_stride + c] = t;
+  }
 }
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int D, int64_t grid, hipStream_t s) {
@@ -568,9 +628,10 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int D, int64_t grid, hipStream_t s)
 hipError_t launch_rab_reduce(const RabReduceArgs& a, hipStream_t s) {
   const int pos_rows = a.d_pos ? (a.pos_stride > 0 ? a.H : 1) : 0;
   const int time_rows = a.d_time ? (a.time_stride > 0 ? a.H : 1) : 0;
-  const int64_t n = (int64_t)pos_rows * a.n_pos + (int64_t)time_rows * a.n_time;
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rab_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, a);
+  if (pos_rows + time_rows == 0) return hipSuccess;
+  const int n = max(pos_rows ? a.n_pos : 0, time_rows ? a.n_time : 0);
+  hipLaunchKernelGGL(rab_reduce_kernel, dim3((unsigned)ceil_div(n, 64), (unsigned)(pos_rows + time_rows)),
+                     dim3(64 * RAB_GROUPS), 0, s, a);
   return hipGetLastError();
 }
 

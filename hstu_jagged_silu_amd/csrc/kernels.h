@@ -121,7 +121,8 @@ struct BwdArgs {
   int64_t T;
   const WorkItem* items;         // scheduler output of the full path
   const int32_t* count;
-  const int32_t* prefix;         // [B+1] first canonical item of each user
+  const int32_t* prefix;         // [B+1] scheduler's item prefix over users (H items per query tile)
+  int32_t B;
   const int64_t* tstats;         // key timestamp ranges per packed 64-row block
   int64_t n_stat_blocks;
   void* dq;                      // [T, H, D] bf16
@@ -131,9 +132,8 @@ struct BwdArgs {
 };
 
 struct RabReduceArgs {
-  const float* part;
-  const int32_t* offsets;
-  const int32_t* prefix;
+  const float* part;             // [H * tiles][RAB_SLOTS], head-major
+  const int32_t* prefix;         // scheduler's item prefix; prefix[B] / H = tiles
   int32_t B, H;
   float* d_pos;                  // like pos_tab: [n_pos] shared or [H][pos_stride]
   int32_t n_pos, pos_stride;

@@ -127,24 +127,40 @@ __global__ __launch_bounds__(64 * LNB_WAVES) void ln_bwd_kernel(LnBwdArgs a) {
   }
 }
 
-// dw[c] = sum over waves of the partials, in wave order
-__global__ __launch_bounds__(256) void ln_affine_reduce_kernel(LnBwdArgs a) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= a.HD) return;
+// dw[c] = sum over waves of the partials. 16 groups of 64 threads split the
+// waves (group g takes waves g, g + 16, ...), then one thread adds the 16
+// group sums in group order: the result does not depend on timing.
+constexpr int RED_GROUPS = 16;
+__global__ __launch_bounds__(64 * RED_GROUPS) void ln_affine_reduce_kernel(LnBwdArgs a) {
+  __shared__ float sw_s[RED_GROUPS][64], sb_s[RED_GROUPS][64];
+  const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + cl;
   float sw = 0.0f, sb = 0.0f;
-  for (int w = 0; a.part && w < a.nwaves; ++w) {
-    sw += a.part[(int64_t)w * a.HD + c];
-    sb += a.part[((int64_t)a.nwaves + w) * a.HD + c];
+  if (c < a.HD && a.part) {
+    for (int w = grp; w < a.nwaves; w += RED_GROUPS) {
+      sw += a.part[(int64_t)w * a.HD + c];
+      sb += a.part[((int64_t)a.nwaves + w) * a.HD + c];
+    }
   }
-  if (a.d_ln_w) a.d_ln_w[c] = sw;
-  if (a.d_ln_b) a.d_ln_b[c] = sb;
+  sw_s[grp][cl] = sw;
+  sb_s[grp][cl] = sb;
+  __syncthreads();
+  if (grp == 0 && c < a.HD) {
+    float tw = 0.0f, tb = 0.0f;
+    for (int g = 0; g < RED_GROUPS; ++g) {
+      tw += sw_s[g][cl];
+      tb += sb_s[g][cl];
+    }
+    if (a.d_ln_w) a.d_ln_w[c] = tw;
+    if (a.d_ln_b) a.d_ln_b[c] = tb;
+  }
 }
 
 hipError_t launch_ln_bwd(const LnBwdArgs& a, hipStream_t s) {
   if (a.HD <= 0) return hipSuccess;
   if (a.T <= 0 || a.nwaves <= 0) {  // no rows: the affine gradients are zero
     if (!a.d_ln_w && !a.d_ln_b) return hipSuccess;
-    hipLaunchKernelGGL(ln_affine_reduce_kernel, dim3((unsigned)ceil_div(a.HD, 256)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(ln_affine_reduce_kernel, dim3((unsigned)ceil_div(a.HD, 64)), dim3(64 * RED_GROUPS), 0, s, a);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)ceil_div(a.nwaves, LNB_WAVES)), blk(64 * LNB_WAVES);
@@ -163,7 +179,7 @@ hipError_t launch_ln_bwd(const LnBwdArgs& a, hipStream_t s) {
   }
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   if (a.d_ln_w || a.d_ln_b)
-    hipLaunchKernelGGL(ln_affine_reduce_kernel, dim3((unsigned)ceil_div(a.HD, 256)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(ln_affine_reduce_kernel, dim3((unsigned)ceil_div(a.HD, 64)), dim3(64 * RED_GROUPS), 0, s, a);
   return hipGetLastError();
 }
 
