@@ -92,7 +92,7 @@ bool layout(int fn, const hstu_params_t* p, int32_t B, int64_t Tq, int64_t max_l
   if (fn == HSTU_FN_FULL_BWD) {
     const bool tables = p->pos_tab || p->time_tab;
     const bool affine = p->ln_w || p->ln_b;
-    w.ln_waves = (int32_t)std::min<int64_t>(ceil_div(Tq, 8), 2048);
+    w.ln_waves = (int32_t)std::min<int64_t>(ceil_div(Tq, 16), 1024);  // row blocks of the norm backward
     w.rab_off = align_up(w.dout_off + (size_t)Tq * (size_t)HD * 2);
     w.lnp_off = align_up(w.rab_off + (tables ? (size_t)w.max_items * RAB_SLOTS * sizeof(float) : 0));
     w.total = align_up(w.lnp_off + (affine ? (size_t)2 * w.ln_waves * (size_t)HD * sizeof(float) : 0));
@@ -294,7 +294,9 @@ hstu_status_t hstu_attn_bwd(const hstu_params_t* params, int32_t batch, const in
   l.du = grads->du;
   l.dout = (char*)ws + w.dout_off;
   l.part = (params->ln_w || params->ln_b) ? (float*)((char*)ws + w.lnp_off) : nullptr;
-  l.nwaves = empty ? 0 : w.ln_waves;
+  // at least 16 rows per block, at most 1024 blocks (partials) in all
+  l.rows_per_block = (int32_t)std::max<int64_t>(16, ceil_div(ceil_div(total_tokens, 1024), 4) * 4);
+  l.nwaves = empty ? 0 : (int32_t)ceil_div(total_tokens, l.rows_per_block);
   l.d_ln_w = grads->d_ln_w;
   l.d_ln_b = grads->d_ln_b;
   if (!mark(1) || launch_ln_bwd(l, stream) != hipSuccess) return HSTU_ERR_LAUNCH;

@@ -24,9 +24,25 @@
 //     registers), then dV^T += dO^T P and dK^T += Q^T dS. The item of query
 //     tile t of a user maps to key block (tiles - 1 - t), whose cost matches.
 // A third kernel adds the per-item histograms in canonical item order.
+#include <type_traits>
+
 #include "tile.h"
 
 namespace hstu {
+
+// time-bucket index z = clz64(|dt| + 1): from the low 32-bit words when the
+// tile's |dt| is known to stay below 2^31 - 2 (the 32-bit difference of the
+// low words is then exact), from the full 64-bit difference otherwise
+template <bool SMALL>
+__device__ inline int time_z(int64_t ta, int64_t tb, int32_t ta_lo, int32_t tb_lo) {
+  if constexpr (SMALL) {
+    const int32_t dt = ta_lo - tb_lo;
+    return __builtin_clz((uint32_t)(dt < 0 ? -dt : dt) + 1u) + 32;
+  } else {
+    const int64_t dt = ta - tb;
+    return __builtin_clzll((uint64_t)(dt < 0 ? -dt : dt) + 1u);
+  }
+}
 
 struct BwdTables {
   float pos_t[BWD_MAX_NPOS];  // -log2(e) * position table
@@ -253,9 +269,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     const bool pos_uniform = (a.pos_tab == nullptr) || (w_lim_min - (j0 + KT - 1) >= n_pos - 1);
     bool time_uniform = !has_time;
     int z_tile = 63;
+    bool small_span = true;
     if (has_time) {
       int64_t k_min, k_max;
       key_time_range(j0, k_min, k_max);
+      const int64_t d1 = w_ts_max - k_min, d2 = k_max - w_ts_min;
+      small_span = max(d1 < 0 ? -d1 : d1, d2 < 0 ? -d2 : d2) < ((int64_t)1 << 31) - 2;
       int64_t lo = -1, hi = -1;
       if (w_ts_min >= k_max) { lo = w_ts_min - k_max; hi = w_ts_max - k_min; }
       else if (k_min >= w_ts_max) { lo = k_min - w_ts_max; hi = k_max - w_ts_min; }
@@ -268,9 +287,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     const float c_uni = (a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f) + (has_time ? tab.time_t[z_tile] : 0.0f);
     const int lim_rel = p_lane - j0 - M::HLK * hl;  // key_of(kb, v, 0) <= lim_rel: allowed
     const int64_t* ts_l = st.ts64 + M::HLK * hl;
+    const int32_t* tsl_lo = st.ts_lo + M::HLK * hl;
+    const int32_t tsq_lo = (int32_t)tsq;
     LB* kl = LDS_PTR(unsigned char, st.k);
     LB* vl = LDS_PTR(unsigned char, st.v);
     float tile_sum = 0.0f;
+    // General path: a lane's keys come in increasing order along v, so with
+    // ordered timestamps its time bucket (and a clamped position bucket)
+    // stays the same over runs of keys. dS' is summed per run and added to
+    // the wave's histogram when the bucket changes, not once per pair.
+    int cur_p = -1, cur_t = -1;
+    float run_p = 0.0f, run_t = 0.0f;
     #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -294,28 +321,46 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
           dsb[v >> 3][v & 7] = (bf16)ds;
         }
       } else {
-        #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kk = M::key_of(kb, v, 0);
-          const bool ok = kk <= lim_rel;
-          const int rel = lim_rel - kk;  // query position - key position
-          const int pb = min((unsigned)rel, (unsigned)(n_pos - 1));
-          float cb = a.pos_tab ? tab.pos_t[pb] : 0.0f;
-          int tb = 0;
-          if (has_time) {
-            const int64_t dt = tsq - ts_l[kk];
-            const int zc = __builtin_clzll((uint64_t)(dt < 0 ? -dt : dt) + 1u);
-            cb += tab.time_t[zc];
-            tb = min(63 - zc, n_time_eff - 1);
+        auto general = [&](auto small_tag) {
+          constexpr bool SMALL = decltype(small_tag)::value;
+          #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int kk = M::key_of(kb, v, 0);
+            const bool ok = kk <= lim_rel;
+            const int rel = lim_rel - kk;  // query position - key position
+            const int pb = min((unsigned)rel, (unsigned)(n_pos - 1));
+            float cb = a.pos_tab ? tab.pos_t[pb] : 0.0f;
+            int tb = 0;
+            if (has_time) {
+              const int zc = time_z<SMALL>(tsq, SMALL ? 0 : ts_l[kk], tsq_lo, SMALL ? tsl_lo[kk] : 0);
+              cb += tab.time_t[zc];
+              tb = min(63 - zc, n_time_eff - 1);
+            }
+            float p, ds;
+            silu_fwd_bwd(ok ? fmaf(s[v], sc, cb) : MASKED_Y, dp[v], p, ds);
+            dsb[v >> 3][v & 7] = (bf16)ds;
+            if (ok && row_ok) {
+              if (a.pos_tab) {
+                if (pb != cur_p) {
+                  if (cur_p >= 0) atomicAdd(&hist.pos[wave][cur_p], run_p);
+                  cur_p = pb;
+                  run_p = 0.0f;
+                }
+                run_p += ds;
+              }
+              if (has_time) {
+                if (tb != cur_t) {
+                  if (cur_t >= 0) atomicAdd(&hist.time[wave][cur_t], run_t);
+                  cur_t = tb;
+                  run_t = 0.0f;
+                }
+                run_t += ds;
+              }
+            }
           }
-          float p, ds;
-          silu_fwd_bwd(ok ? fmaf(s[v], sc, cb) : MASKED_Y, dp[v], p, ds);
-          dsb[v >> 3][v & 7] = (bf16)ds;
-          if (ok && row_ok) {
-            if (a.pos_tab) atomicAdd(&hist.pos[wave][pb], ds);
-            if (has_time) atomicAdd(&hist.time[wave][tb], ds);
-          }
-        }
+        };
+        if (small_span) general(std::true_type{});
+        else general(std::false_type{});
       }
       // dQ^T += K^T dS^T for the 32 keys of block kb
       #pragma unroll
@@ -330,6 +375,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
+    if (cur_p >= 0) atomicAdd(&hist.pos[wave][cur_p], run_p);
+    if (cur_t >= 0) atomicAdd(&hist.time[wave][cur_t], run_t);
     if (fast) {
       // rows past q_len have zero dO, so their dS' is 0 and they add nothing
       const float tot = wave_sum_f(tile_sum);
@@ -473,15 +520,20 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
     const bool pos_uniform = (a.pos_tab == nullptr) || (j0 - w_kmax >= n_pos - 1);
     bool time_uniform = !has_time;
     int z_tile = 63;
-    if (has_time && !need_mask && pos_uniform) {
+    bool small_span = true;
+    if (has_time) {
       const int64_t r0 = q_off + j0;
       const int64_t i0 = min(r0 / KT, a.n_stat_blocks - 1), i1 = min((r0 + KT - 1) / KT, a.n_stat_blocks - 1);
-      const int64_t q_min = min(ldc(a.tstats + 2 * i0), ldc(a.tstats + 2 * i1));
-      const int64_t q_max = max(ldc(a.tstats + 2 * i0 + 1), ldc(a.tstats + 2 * i1 + 1));
+      int64_t q_min = min(ldc(a.tstats + 2 * i0), ldc(a.tstats + 2 * i1));
+      int64_t q_max = max(ldc(a.tstats + 2 * i0 + 1), ldc(a.tstats + 2 * i1 + 1));
+      if (q_min > q_max) q_min = q_max = w_ts_min;
+      // rows past the user's end (last tile) are clamped copies of its last row
+      const int64_t d1 = q_max - w_ts_min, d2 = w_ts_max - q_min;
+      small_span = max(d1 < 0 ? -d1 : d1, d2 < 0 ? -d2 : d2) < ((int64_t)1 << 31) - 2;
       int64_t lo = -1, hi = -1;
       if (q_min >= w_ts_max) { lo = q_min - w_ts_max; hi = q_max - w_ts_min; }
       else if (w_ts_min >= q_max) { lo = w_ts_min - q_max; hi = w_ts_max - q_min; }
-      if (lo >= 0) {
+      if (lo >= 0 && !need_mask && pos_uniform) {
         const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
         if (min(63 - zlo, n_time_eff - 1) == min(63 - zhi, n_time_eff - 1)) { time_uniform = true; z_tile = zlo; }
       }
@@ -489,6 +541,8 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
     const bool fast = pos_uniform && time_uniform && !need_mask;
     const float c_uni = (a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f) + (has_time ? tab.time_t[z_tile] : 0.0f);
     const int64_t* ts_l = st.ts64 + M::HLK * hl;
+    const int32_t* tsl_lo = st.ts_lo + M::HLK * hl;
+    const int32_t tsk_lo = (int32_t)tsk;
     LB* ql = LDS_PTR(unsigned char, st.k);
     LB* gl = LDS_PTR(unsigned char, st.v);
     #pragma unroll
@@ -515,22 +569,27 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
           dsb[v >> 3][v & 7] = (bf16)ds;
         }
       } else {
-        #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int ql_ = M::key_of(qb, v, hl);  // query row within the tile
-          const int qpos = j0 + ql_;
-          const bool ok = key_ok && qpos >= kpos && qpos < L;
-          const int rel = qpos - kpos;
-          float cb = a.pos_tab ? tab.pos_t[min((unsigned)rel, (unsigned)(n_pos - 1))] : 0.0f;
-          if (has_time) {
-            const int64_t dt = ts_l[M::key_of(qb, v, 0)] - tsk;
-            cb += tab.time_t[__builtin_clzll((uint64_t)(dt < 0 ? -dt : dt) + 1u)];
+        auto general = [&](auto small_tag) {
+          constexpr bool SMALL = decltype(small_tag)::value;
+          #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int ql_ = M::key_of(qb, v, hl);  // query row within the tile
+            const int qpos = j0 + ql_;
+            const bool ok = key_ok && qpos >= kpos && qpos < L;
+            const int rel = qpos - kpos;
+            float cb = a.pos_tab ? tab.pos_t[min((unsigned)rel, (unsigned)(n_pos - 1))] : 0.0f;
+            if (has_time) {
+              const int qv = M::key_of(qb, v, 0);
+              cb += tab.time_t[time_z<SMALL>(SMALL ? 0 : ts_l[qv], tsk, SMALL ? tsl_lo[qv] : 0, tsk_lo)];
+            }
+            float p, ds;
+            silu_fwd_bwd(ok ? fmaf(s[v], sc, cb) : MASKED_Y, dp[v], p, ds);
+            pb[v >> 3][v & 7] = (bf16)p;
+            dsb[v >> 3][v & 7] = (bf16)ds;
           }
-          float p, ds;
-          silu_fwd_bwd(ok ? fmaf(s[v], sc, cb) : MASKED_Y, dp[v], p, ds);
-          pb[v >> 3][v & 7] = (bf16)p;
-          dsb[v >> 3][v & 7] = (bf16)ds;
-        }
+        };
+        if (small_span) general(std::true_type{});
+        else general(std::false_type{});
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries of block qb
       #pragma unroll

@@ -155,7 +155,8 @@ struct LnBwdArgs {
   void* du;                      // [T, HD], dtype of u
   void* dout;                    // [T, HD] bf16
   float* part;                   // [2][nwaves][HD] (dw, db), or null
-  int32_t nwaves;
+  int32_t nwaves;                // row blocks, one partial each
+  int32_t rows_per_block;
   float* d_ln_w;
   float* d_ln_b;
 };

@@ -7,16 +7,18 @@
 // follow "How Generative Recommenders Are Redefining RecSys at Scale",
 // Takeaways (elementwise gating before the output projection).
 //
-// One wave64 per row at a time; each wave walks rows with a grid-wide stride
-// and keeps its share of dw and db in registers, written once as a per-wave
-// partial. A second kernel adds the partials in wave order (reproducible).
+// A workgroup of four waves owns a.rows_per_block consecutive rows (one wave
+// per row at a time); each wave keeps its share of dw and db in registers, the four
+// are added in wave order through LDS and written once as the workgroup's
+// partial. A second kernel adds the partials in a fixed order, so the result
+// does not depend on timing.
 // HBM-bound: per element it reads O (4 B), U and dY (2 B each) and writes dU
 // and dO (2 B each).
 #include "kernels.h"
 
 namespace hstu {
 
-constexpr int LNB_WAVES = 4;  // waves per workgroup
+constexpr int LNB_WAVES = 4;   // waves per workgroup
 
 __device__ inline float lnb_wave_sum(float x) {
   for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
@@ -38,8 +40,7 @@ __device__ inline void st_bf4(bf16* p, f32x4 x) {
 template <int NCH, bool FULL_LANES>
 __global__ __launch_bounds__(64 * LNB_WAVES) void ln_bwd_kernel(LnBwdArgs a) {
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * LNB_WAVES + (threadIdx.x >> 6);
-  if (wave >= a.nwaves) return;
+  const int wave = threadIdx.x >> 6;
   const int nch = a.HD / 4;
   bool on[NCH];
   int col[NCH];
@@ -55,7 +56,8 @@ __global__ __launch_bounds__(64 * LNB_WAVES) void ln_bwd_kernel(LnBwdArgs a) {
     db[i] = f32x4{0, 0, 0, 0};
   }
   const float inv_hd = 1.0f / (float)a.HD;
-  for (int64_t row = wave; row < a.T; row += a.nwaves) {
+  const int64_t row_end = min<int64_t>(a.T, (int64_t)(blockIdx.x + 1) * a.rows_per_block);
+  for (int64_t row = (int64_t)blockIdx.x * a.rows_per_block + wave; row < row_end; row += LNB_WAVES) {
     const float* orow = a.o + row * a.HD;
     const bf16* urow = (const bf16*)a.u + row * a.HD;
     const bf16* yrow = (const bf16*)a.dy + row * a.HD;
@@ -115,21 +117,37 @@ __global__ __launch_bounds__(64 * LNB_WAVES) void ln_bwd_kernel(LnBwdArgs a) {
       st_bf4(dorow + col[i], d);
     }
   }
-  if (a.part) {
-    float* pw = a.part + (int64_t)wave * a.HD;
-    float* pb = a.part + ((int64_t)a.nwaves + wave) * a.HD;
+  if (!a.part) return;
+  // add the four waves' shares in wave order: waves 1..3 stage, wave 0 adds
+  __shared__ f32x4 stage[LNB_WAVES - 1][2][NCH][64];
+  if (wave > 0) {
     #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      if (!on[i]) continue;
-      *(f32x4*)(pw + col[i]) = dw[i];
-      *(f32x4*)(pb + col[i]) = db[i];
+      stage[wave - 1][0][i][lane] = dw[i];
+      stage[wave - 1][1][i][lane] = db[i];
     }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float* pw = a.part + (int64_t)blockIdx.x * a.HD;
+  float* pb = a.part + ((int64_t)a.nwaves + blockIdx.x) * a.HD;
+  #pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    if (!on[i]) continue;
+    f32x4 w_ = dw[i], b_ = db[i];
+    #pragma unroll
+    for (int k = 0; k < LNB_WAVES - 1; ++k) {
+      w_ += stage[k][0][i][lane];
+      b_ += stage[k][1][i][lane];
+    }
+    *(f32x4*)(pw + col[i]) = w_;
+    *(f32x4*)(pb + col[i]) = b_;
   }
 }
 
-// dw[c] = sum over waves of the partials. 16 groups of 64 threads split the
-// waves (group g takes waves g, g + 16, ...), then one thread adds the 16
-// group sums in group order: the result does not depend on timing.
+// dw[c] = sum over workgroups of the partials. 16 groups of 64 threads split
+// them (group g takes partials g, g + 16, ...), then one thread adds the 16
+// group sums in group order.
 constexpr int RED_GROUPS = 16;
 __global__ __launch_bounds__(64 * RED_GROUPS) void ln_affine_reduce_kernel(LnBwdArgs a) {
   __shared__ float sw_s[RED_GROUPS][64], sb_s[RED_GROUPS][64];
@@ -163,7 +181,7 @@ hipError_t launch_ln_bwd(const LnBwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(ln_affine_reduce_kernel, dim3((unsigned)ceil_div(a.HD, 64)), dim3(64 * RED_GROUPS), 0, s, a);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)ceil_div(a.nwaves, LNB_WAVES)), blk(64 * LNB_WAVES);
+  const dim3 grid((unsigned)a.nwaves), blk(64 * LNB_WAVES);
   switch (a.HD) {
     case 256: hipLaunchKernelGGL((ln_bwd_kernel<1, true>), grid, blk, 0, s, a); break;
     case 512: hipLaunchKernelGGL((ln_bwd_kernel<2, true>), grid, blk, 0, s, a); break;
