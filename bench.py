@@ -370,6 +370,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-variants", action="store_true", help="time only the headline workload")
+    ap.add_argument("--variants", default="", help="comma-separated subset of the variants to run (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=8192)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -453,6 +454,8 @@ def main():
                          ("jagged_training_shape", bench_training_shape), ("full_layer", bench_layer),
                          ("backward_training_shape", bench_backward_training),
                          ("backward_causal_B8_L8192", bench_backward_long)):
+            if args.variants and name not in args.variants.split(","):
+                continue
             log(f"variant {name}")
             variants[name] = fn(torch, hs, W, args.steps, args.warmup)
             log(f"  {variants[name]}")
