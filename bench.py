@@ -302,8 +302,8 @@ def bench_backward_long(torch, hs, W, steps, warmup):
     return _bench_backward(torch, hs, W, W.long_seq(), steps, warmup)
 
 
-def bench_layer(torch, hs, W, steps, warmup):
-    """Full layer: f1 + SiLU (4 hipBLASLt products), attention, f2."""
+def bench_layer(torch, hs, W, steps, warmup, products=0):
+    """Full layer: f1 + SiLU (hipBLASLt, or the library's own MFMA product), attention, f2."""
     inp = W.full_layer()
     bf = torch.bfloat16
     H, d, E = inp.num_heads, inp.head_dim, inp.x.shape[1]
@@ -314,7 +314,8 @@ def bench_layer(torch, hs, W, steps, warmup):
     out = torch.empty_like(x)
     ws = torch.empty(hs.hstu_layer_workspace_size(p, E, len(inp.lengths), inp.total, inp.max_len), dtype=torch.uint8,
                      device="cuda")
-    fn = lambda ev: hs.hstu_layer_fwd(x, w1, w2, ts, off, inp.max_len, p, out=out, workspace=ws, timing_events=ev)
+    fn = lambda ev: hs.hstu_layer_fwd(x, w1, w2, ts, off, inp.max_len, p, out=out, workspace=ws, timing_events=ev,
+                                      products=products)
     ms, evs = timed(fn, steps, warmup, torch)
     T, HD = inp.total, H * d
     f1_flop, f2_flop = 2 * T * E * 4 * HD, 2 * T * HD * E
@@ -322,6 +323,7 @@ def bench_layer(torch, hs, W, steps, warmup):
     f1_ms, attn_ms, f2_ms = mean_span(evs, 0, 1), mean_span(evs, 1, 2), mean_span(evs, 2, 3)
     return {
         "workload": inp.name,
+        "products": "own MFMA kernel" if products else "hipBLASLt",
         "total_tokens": T,
         "ms_per_step": round(ms, 4),
         "tflops": round((f1_flop + f2_flop + attn_flop) / (ms * 1e-3) / 1e12, 2),
@@ -452,6 +454,8 @@ def main():
         for name, fn in (("kv_cache_delta", bench_cached), ("mfalcon", bench_mfalcon),
                          ("mfalcon_paged_history", bench_mfalcon_paged),
                          ("jagged_training_shape", bench_training_shape), ("full_layer", bench_layer),
+                         ("full_layer_own_products",
+                          lambda torch, hs, W, st, wu: bench_layer(torch, hs, W, st, wu, products=1)),
                          ("backward_training_shape", bench_backward_training),
                          ("backward_causal_B8_L8192", bench_backward_long)):
             if args.variants and name not in args.variants.split(","):

@@ -33,7 +33,7 @@ PAGE_SIZE = 64
 EXPORTED_SYMBOLS = (
     "hstu_status_string", "hstu_version", "hstu_workspace_size", "hstu_attn_fwd",
     "hstu_kv_append", "hstu_attn_fwd_cached", "hstu_mfalcon_fwd", "hstu_mfalcon_fwd_cached", "hstu_attn_bwd",
-    "hstu_layer_workspace_size",
+    "hstu_layer_workspace_size", "hstu_matmul_bf16",
     "hstu_layer_fwd", "hstu_pm_create", "hstu_pm_destroy", "hstu_pm_reserve", "hstu_pm_commit", "hstu_pm_lookup",
     "hstu_pm_evict", "hstu_pm_stats",
 )
@@ -69,7 +69,11 @@ class _Grads(ctypes.Structure):
 
 
 class _LayerWeights(ctypes.Structure):
-    _fields_ = [("embed_dim", ctypes.c_int32), ("w1", ctypes.c_void_p), ("w2", ctypes.c_void_p)]
+    _fields_ = [("embed_dim", ctypes.c_int32), ("w1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("products", ctypes.c_int32)]
+
+
+HSTU_PRODUCTS_HIPBLASLT, HSTU_PRODUCTS_OWN = 0, 1
 
 
 def _load():
@@ -90,6 +94,8 @@ def _load():
     lib.hstu_attn_fwd.argtypes = [P, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hstu_attn_bwd.restype = ctypes.c_int
     lib.hstu_attn_bwd.argtypes = [P, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp, ctypes.POINTER(_Grads), vp, sz, vp]
+    lib.hstu_matmul_bf16.restype = ctypes.c_int
+    lib.hstu_matmul_bf16.argtypes = [i64, i32, i32, vp, vp, vp, i32, i32, vp]
     lib.hstu_kv_append.restype = ctypes.c_int
     lib.hstu_kv_append.argtypes = [K, P, i32, vp, vp, i64, vp, vp, vp, vp]
     lib.hstu_attn_fwd_cached.restype = ctypes.c_int
@@ -314,6 +320,29 @@ def hstu_mfalcon_fwd(q, k, v, u, ts, seq_offsets, num_candidates, max_len: int, 
     return y
 
 
+HSTU_EPI_NONE, HSTU_EPI_SILU_SPLIT = 0, 1
+
+
+def hstu_matmul_bf16(a, b, *, epilogue: int = HSTU_EPI_NONE, split_width: int = 0, out=None):
+    """C = A B on the library's MFMA kernel (bf16). a [M, K], b [K, N].
+    HSTU_EPI_NONE returns [M, N]; HSTU_EPI_SILU_SPLIT returns [N / w, M, w]
+    (SiLU, then column blocks of width w = split_width)."""
+    _device_tensor(a, torch.bfloat16, "a")
+    _device_tensor(b, torch.bfloat16, "b")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError("a must be [M, K] and b [K, N]")
+    M, K = a.shape
+    N = b.shape[1]
+    shape = (M, N) if epilogue == HSTU_EPI_NONE else (N // max(split_width, 1), M, split_width)
+    out = torch.empty(shape, dtype=torch.bfloat16, device=a.device) if out is None else out
+    _device_tensor(out, torch.bfloat16, "out")
+    if out.numel() != M * N:
+        raise ValueError("out has the wrong size")
+    _check(_lib.hstu_matmul_bf16(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), epilogue, split_width,
+                                 _stream()), "hstu_matmul_bf16")
+    return out
+
+
 def hstu_layer_workspace_size(params: LayerParams, embed_dim: int, batch: int, total_tokens: int,
                               max_len: int) -> int:
     """Workspace bytes of one hstu_layer_fwd call."""
@@ -325,11 +354,12 @@ def hstu_layer_workspace_size(params: LayerParams, embed_dim: int, batch: int, t
 
 
 def hstu_layer_fwd(x, w1, w2, ts, seq_offsets, max_len: int, params: LayerParams, *, out=None,
-                   workspace=None, timing_events=None):
+                   workspace=None, timing_events=None, products: int = HSTU_PRODUCTS_HIPBLASLT):
     """Full layer: [U|V|Q|K] = SiLU(x w1), attention, out = A w2.
 
     x [T, E], w1 [E, 4*H*d], w2 [H*d, E], all bf16 on the GPU; ts int64 [T];
-    seq_offsets int32 [B+1]. Returns out [T, E]."""
+    seq_offsets int32 [B+1]. products: HSTU_PRODUCTS_HIPBLASLT or
+    HSTU_PRODUCTS_OWN (the library's MFMA kernel). Returns out [T, E]."""
     H, d = params.num_heads, params.head_dim
     for name, t in (("x", x), ("w1", w1), ("w2", w2)):
         _device_tensor(t, params.dtype, name)
@@ -348,7 +378,7 @@ def hstu_layer_fwd(x, w1, w2, ts, seq_offsets, max_len: int, params: LayerParams
     nbytes = hstu_layer_workspace_size(params, E, B, T, max_len)
     ws = _workspace(workspace, nbytes, x.device)
     p = params.c_struct(timing_events)
-    wts = _LayerWeights(E, w1.data_ptr(), w2.data_ptr())
+    wts = _LayerWeights(E, w1.data_ptr(), w2.data_ptr(), products)
     _check(_lib.hstu_layer_fwd(ctypes.byref(p), ctypes.byref(wts), B, seq_offsets.data_ptr(), max_len, T,
                                x.data_ptr(), ts.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
            "hstu_layer_fwd")

@@ -7,10 +7,12 @@
 // "Generative recommenders at scale", section "Inside NVIDIA's GPU-native
 // stack for HSTU and Semantic IDs".
 //
-// The two products are plain dense GEMMs and run on hipBLASLt; f1's SiLU is
-// its SWISH epilogue, applied to the fp32 accumulator before the bf16 store.
-// f1 runs as one product per column block of W1 (U, V, Q, K) so that each
-// lands packed as [T, H*d], the layout the attention kernels read.
+// The two products are plain dense GEMMs. They run on hipBLASLt (f1's SiLU
+// is its SWISH epilogue, applied to the fp32 accumulator before the bf16
+// store; f1 runs as one product per column block of W1, U, V, Q, K, so that
+// each lands packed as [T, H*d], the layout the attention kernels read) or,
+// when the caller asks for it, on this library's own MFMA kernel (gemm.hip),
+// which does f1 as one product with the SiLU and the split in its epilogue.
 //
 // hipBLASLt works on column-major matrices. A row-major [R, C] matrix is the
 // column-major [C, R] matrix with leading dimension C, so the row-major
@@ -25,6 +27,7 @@
 #include <vector>
 
 #include "../../include/hstu.h"
+#include "gemm.h"
 
 namespace {
 
@@ -183,6 +186,13 @@ hstu_status_t hstu_layer_fwd(const hstu_params_t* params, const hstu_layer_weigh
   if (params->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
   if (batch < 0 || total_tokens < 0 || max_len < 0 || weights->embed_dim < 1 || (weights->embed_dim % 8) != 0)
     return HSTU_ERR_INVALID_ARG;
+  if (weights->products != HSTU_PRODUCTS_HIPBLASLT && weights->products != HSTU_PRODUCTS_OWN)
+    return HSTU_ERR_INVALID_ARG;
+  const bool own = weights->products == HSTU_PRODUCTS_OWN;
+  if (own) {
+    const int64_t hd = (int64_t)params->num_heads * params->head_dim, e = weights->embed_dim;
+    if ((4 * hd) % 256 != 0 || e % 256 != 0 || e % 64 != 0 || hd % 64 != 0) return HSTU_ERR_UNSUPPORTED;
+  }
   // the attention checks the remaining parameters; run them before anything is launched
   if (hstu_workspace_size(HSTU_FN_FULL, params, batch, total_tokens, max_len) == 0) return HSTU_ERR_INVALID_ARG;
   if (batch == 0 || total_tokens == 0) return HSTU_OK;
@@ -208,12 +218,30 @@ hstu_status_t hstu_layer_fwd(const hstu_params_t* params, const hstu_layer_weigh
   void* a = base + w.a_off;
   void* gws = base + w.gemm_off;
 
-  // f1 with SiLU, one column block of W1 at a time: U, V, Q, K
+  // f1 with SiLU into U, V, Q, K
   if (!mark(0)) return HSTU_ERR_LAUNCH;
   const char* w1 = (const char*)weights->w1;
-  for (int i = 0; i < 4; ++i) {
-    hstu_status_t st = gemm_bf16(dev, HD, T, E, w1 + (size_t)i * HD * 2, 4 * HD, x, E, bufs[i], HD, true, gws, stream);
-    if (st != HSTU_OK) return st;
+  if (own) {
+    // one product; the epilogue writes column block i to buffer i (the
+    // buffers sit buf_elems apart in the workspace)
+    hstu::GemmArgs g = {};
+    g.a = (const hstu::bf16*)x;
+    g.b = (const hstu::bf16*)weights->w1;
+    g.c = (hstu::bf16*)bufs[0];
+    g.M = T;
+    g.N = (int32_t)(4 * HD);
+    g.K = (int32_t)E;
+    g.mt_count = (T + 255) / 256;
+    g.epilogue = hstu::GEMM_EPI_SILU_SPLIT;
+    g.split = (int32_t)HD;
+    g.split_stride = (int64_t)(w.uvqk_off[1] - w.uvqk_off[0]) / 2;
+    if (hstu::launch_gemm(g, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  } else {
+    for (int i = 0; i < 4; ++i) {
+      hstu_status_t st =
+          gemm_bf16(dev, HD, T, E, w1 + (size_t)i * HD * 2, 4 * HD, x, E, bufs[i], HD, true, gws, stream);
+      if (st != HSTU_OK) return st;
+    }
   }
   if (!mark(1)) return HSTU_ERR_LAUNCH;
 
@@ -225,10 +253,49 @@ hstu_status_t hstu_layer_fwd(const hstu_params_t* params, const hstu_layer_weigh
   if (!mark(2)) return HSTU_ERR_LAUNCH;
 
   // f2: out = A W2
-  st = gemm_bf16(dev, E, T, HD, weights->w2, E, a, HD, out, E, false, gws, stream);
-  if (st != HSTU_OK) return st;
+  if (own) {
+    hstu::GemmArgs g = {};
+    g.a = (const hstu::bf16*)a;
+    g.b = (const hstu::bf16*)weights->w2;
+    g.c = (hstu::bf16*)out;
+    g.M = T;
+    g.N = (int32_t)E;
+    g.K = (int32_t)HD;
+    g.mt_count = (T + 255) / 256;
+    g.epilogue = hstu::GEMM_EPI_NONE;
+    g.split = (int32_t)E;
+    g.split_stride = 0;
+    if (hstu::launch_gemm(g, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  } else {
+    st = gemm_bf16(dev, E, T, HD, weights->w2, E, a, HD, out, E, false, gws, stream);
+    if (st != HSTU_OK) return st;
+  }
   if (!mark(3)) return HSTU_ERR_LAUNCH;
   return HSTU_OK;
 }
 
 }  // extern "C"
+
+extern "C" hstu_status_t hstu_matmul_bf16(int64_t M, int32_t N, int32_t K, const void* a, const void* b, void* c,
+                                          int32_t epilogue, int32_t split_width, hipStream_t stream) {
+  if (M < 0 || N <= 0 || K <= 0) return HSTU_ERR_INVALID_ARG;
+  if (epilogue != HSTU_EPI_NONE && epilogue != HSTU_EPI_SILU_SPLIT) return HSTU_ERR_INVALID_ARG;
+  if (N % 256 != 0 || K % 64 != 0) return HSTU_ERR_UNSUPPORTED;
+  if (epilogue == HSTU_EPI_SILU_SPLIT && (split_width <= 0 || split_width % 32 != 0 || N % split_width != 0))
+    return HSTU_ERR_UNSUPPORTED;
+  if ((M + 255) / 256 * (int64_t)(N / 256) > INT32_MAX) return HSTU_ERR_UNSUPPORTED;
+  if (M == 0) return HSTU_OK;
+  if (!a || !b || !c || !aligned16(a) || !aligned16(b) || !aligned16(c)) return HSTU_ERR_INVALID_ARG;
+  hstu::GemmArgs g = {};
+  g.a = (const hstu::bf16*)a;
+  g.b = (const hstu::bf16*)b;
+  g.c = (hstu::bf16*)c;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.mt_count = (M + 255) / 256;
+  g.epilogue = epilogue == HSTU_EPI_SILU_SPLIT ? hstu::GEMM_EPI_SILU_SPLIT : hstu::GEMM_EPI_NONE;
+  g.split = epilogue == HSTU_EPI_SILU_SPLIT ? split_width : N;
+  g.split_stride = M * (int64_t)g.split;
+  return hstu::launch_gemm(g, stream) == hipSuccess ? HSTU_OK : HSTU_ERR_LAUNCH;
+}

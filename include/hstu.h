@@ -354,10 +354,13 @@ hstu_status_t hstu_pm_stats(hstu_page_manager_t* pm, int32_t* free_pages, int32_
  *   A = hstu_attn_fwd(Q, K, V, U, ts)   the full causal path above
  *   out = A W2                          W2 [HD, E], out [T, E]
  *
- * f1 and f2 have no bias term. The two products run on hipBLASLt (f1 with
- * its SiLU epilogue, one product per U/V/Q/K column block, each writing a
- * packed [T, HD] buffer in the workspace); the attention runs on this
- * library's kernels. Only HSTU_BF16 is supported (HSTU_ERR_UNSUPPORTED for
+ * f1 and f2 have no bias term. weights->products picks where the two
+ * products run: HSTU_PRODUCTS_HIPBLASLT (0, f1 with its SiLU epilogue, one
+ * product per U/V/Q/K column block, each writing a packed [T, HD] buffer in
+ * the workspace) or HSTU_PRODUCTS_OWN (1, hstu_matmul_bf16: f1 as one
+ * product with SiLU and the U/V/Q/K split fused in its epilogue; needs
+ * 4*H*d and E multiples of 256 and E and H*d multiples of 64, else
+ * HSTU_ERR_UNSUPPORTED). The attention runs on this library's kernels. Only HSTU_BF16 is supported (HSTU_ERR_UNSUPPORTED for
  * HSTU_F32): bf16 operands, fp32 accumulation, bf16 U, V, Q, K, A and out.
  *   weights->w1, weights->w2  row-major device matrices in bf16
  *   x    [T, E] bf16; ts int64 [T]; out [T, E] bf16 (must not alias x)
@@ -368,11 +371,36 @@ hstu_status_t hstu_pm_stats(hstu_page_manager_t* pm, int32_t* free_pages, int32_
  * host state the library holds); later calls reuse it and the chosen GEMM
  * algorithms. Callable from several host threads.
  */
+typedef enum { HSTU_PRODUCTS_HIPBLASLT = 0, HSTU_PRODUCTS_OWN = 1 } hstu_products_t;
+
 typedef struct {
   int32_t embed_dim;  /* E >= 1, multiple of 8 */
   const void* w1;     /* [E, 4 * H * d] */
   const void* w2;     /* [H * d, E] */
+  int32_t products;   /* hstu_products_t */
 } hstu_layer_weights_t;
+
+/* Epilogues of hstu_matmul_bf16. */
+typedef enum { HSTU_EPI_NONE = 0, HSTU_EPI_SILU_SPLIT = 1 } hstu_epilogue_t;
+
+/*
+ * The layer's dense product on the library's own MFMA kernel: C = A B with
+ * A [M, K] and B [K, N] row-major bf16, fp32 accumulation, bf16 output.
+ * Epilogues (the layer's f1 and f2: a pointwise projection with SiLU that
+ * produces U, V, Q, K, and the output projection, "How Generative
+ * Recommenders Are Redefining RecSys at Scale", Takeaways):
+ *   HSTU_EPI_NONE        C is [M, N].
+ *   HSTU_EPI_SILU_SPLIT  SiLU of every entry, then columns are split into
+ *                        N / split_width blocks written one after another,
+ *                        block i = columns [i*w, (i+1)*w) as [M, w]
+ *                        (w = split_width; U, V, Q, K for w = H*d, N = 4w).
+ * N must be a multiple of 256 and K of 64 (else HSTU_ERR_UNSUPPORTED);
+ * split_width a multiple of 32 dividing N. M >= 0 (M = 0 does nothing).
+ * Pointers 16-byte aligned; C must not alias A or B. No workspace; runs on
+ * `stream`, allocates nothing.
+ */
+hstu_status_t hstu_matmul_bf16(int64_t M, int32_t N, int32_t K, const void* a, const void* b, void* c,
+                               int32_t epilogue, int32_t split_width, hipStream_t stream);
 
 /* Workspace bytes of hstu_layer_fwd; 0 for invalid arguments. Monotone in
  * every argument like hstu_workspace_size. */

@@ -60,7 +60,7 @@ __all__ = [
     "time_bucket", "pos_bucket", "silu", "layer_norm_gate",
     "hstu_full", "hstu_full_rows", "hstu_cached", "hstu_mfalcon",
     "kv_append_pages", "hstu_layer", "max_rel_row_error", "pair_count",
-    "silu_grad", "layer_norm_gate_bwd", "hstu_full_bwd", "max_rel_err_vs_magnitude",
+    "silu_grad", "layer_norm_gate_bwd", "hstu_full_bwd", "max_rel_err_vs_magnitude", "dense",
 ]
 
 
@@ -336,6 +336,19 @@ def hstu_mfalcon(q, k, v, u, ts, seq_offsets, num_candidates, pos_tab=None, time
 # ----------------------------------------------------------------------------
 # Full HSTU layer around the attention
 # ----------------------------------------------------------------------------
+
+def dense(a, b, apply_silu=False, split_width=None):
+    """One of the layer's dense products: a @ b in float64, then SiLU if asked
+    (f1 is SiLU(X W1), f2 is a plain product; "How Generative Recommenders Are
+    Redefining RecSys at Scale", Takeaways). With split_width w the columns
+    are returned as the list of blocks [i*w, (i+1)*w) (U, V, Q, K for f1)."""
+    c = np.asarray(a, dtype=np.float64) @ np.asarray(b, dtype=np.float64)
+    if apply_silu:
+        c = silu(c)
+    if split_width is None:
+        return c
+    return [c[:, i:i + split_width] for i in range(0, c.shape[1], split_width)]
+
 
 def hstu_layer(x, w1, w2, ts, seq_offsets, num_heads, head_dim, pos_tab=None, time_tab=None, alpha=1.0,
                gamma=None, beta=None, eps=1e-5, rows=None):

@@ -61,6 +61,7 @@ int main(void) {
   P(hstu_grads_t, d_pos_tab); P(hstu_grads_t, d_time_tab); P(hstu_grads_t, d_ln_w); P(hstu_grads_t, d_ln_b);
   printf("hstu_layer_weights_t %zu\n", sizeof(hstu_layer_weights_t));
   P(hstu_layer_weights_t, embed_dim); P(hstu_layer_weights_t, w1); P(hstu_layer_weights_t, w2);
+  P(hstu_layer_weights_t, products);
   return 0;
 }
 ''')
@@ -204,6 +205,8 @@ def test_layer_workspace_and_bad_arguments_before_launch():
     assert call(_params(dtype=0)) == UNSUPPORTED
     assert call(p, w=hs._LayerWeights(1020, FAKE, FAKE)) == INVALID
     assert call(p, w=hs._LayerWeights(1024, None, FAKE)) == INVALID
+    assert call(p, w=hs._LayerWeights(1024, FAKE, FAKE, 2)) == INVALID       # unknown product backend
+    assert call(p, w=hs._LayerWeights(1000, FAKE, FAKE, 1)) == UNSUPPORTED   # own products need E % 256 == 0
     assert call(p, x=None) == INVALID
     assert call(p, x=FAKE + 2) == INVALID
     assert call(_params(head_dim=48)) == INVALID
@@ -259,6 +262,20 @@ def test_backward_workspace_and_bad_arguments_before_launch():
     assert call(q=FAKE + 4, wsb=1 << 40) == INVALID
     assert call(p=_params(head_dim=48)) == UNSUPPORTED
     assert call(B=0, wsb=1 << 40) == OK      # nothing to compute and no table or affine gradient requested
+
+
+def test_matmul_rejects_bad_arguments_before_launch():
+    f = hs.lib().hstu_matmul_bf16
+    call = lambda M=512, N=256, K=64, a=FAKE, epi=0, w=0: f(M, N, K, a, FAKE, FAKE, epi, w, None)
+    assert call(N=100) == UNSUPPORTED
+    assert call(K=96) == UNSUPPORTED
+    assert call(M=-1) == INVALID
+    assert call(epi=7) == INVALID
+    assert call(epi=1, w=48) == UNSUPPORTED
+    assert call(epi=1, w=96) == UNSUPPORTED      # does not divide N
+    assert call(a=None) == INVALID
+    assert call(a=FAKE + 2) == INVALID
+    assert call(M=0) == OK
 
 
 def test_pair_count_matches_closed_forms():

@@ -13,6 +13,9 @@ from devutil import TOL, dev, to_np
 pytestmark = pytest.mark.gpu
 
 
+PRODUCTS = [hs.HSTU_PRODUCTS_HIPBLASLT, hs.HSTU_PRODUCTS_OWN]
+
+
 def run_layer(inp, **kw):
     bf = torch.bfloat16
     p = hs.LayerParams(num_heads=inp.num_heads, head_dim=inp.head_dim, dtype=bf,
@@ -23,9 +26,10 @@ def run_layer(inp, **kw):
     return to_np(out)
 
 
-def test_small_layer_all_rows():
+@pytest.mark.parametrize("products", PRODUCTS)
+def test_small_layer_all_rows(products):
     inp = W.full_layer(seed=21, batch=4, embed=256, num_heads=2, head_dim=128, lengths=[1, 77, 200, 130])
-    y = run_layer(inp)
+    y = run_layer(inp, products=products)
     y_ref = oracle.hstu_layer(inp.x, inp.w1, inp.w2, inp.ts, inp.seq_offsets, inp.num_heads, inp.head_dim,
                               inp.tables.pos, inp.tables.time)
     err = oracle.max_rel_row_error(y, y_ref)
@@ -41,10 +45,11 @@ def test_layer_head_dim_64_and_empty_user():
     assert oracle.max_rel_row_error(y, y_ref) <= TOL["bf16"]
 
 
-def test_full_size_layer_sampled_rows():
+@pytest.mark.parametrize("products", PRODUCTS)
+def test_full_size_layer_sampled_rows(products):
     """Batch 16, lognormal lengths (median 2,048) capped at 8,192, E = 1,024, 8 x 128: sampled rows."""
     inp = W.full_layer()
-    y = run_layer(inp)
+    y = run_layer(inp, products=products)
     assert np.isfinite(y).all()
     off = inp.seq_offsets
     rng = np.random.default_rng(11)

@@ -435,3 +435,19 @@ def test_pair_counts():
     # brute force over tiny masks
     L = 7
     assert oracle.pair_count("full", [L]) == sum(1 for i in range(L) for j in range(L) if j <= i)
+
+
+def test_dense_matches_loops_and_split_order():
+    rng = np.random.default_rng(5)
+    a = rng.integers(-3, 4, size=(5, 4)).astype(np.float64)
+    b = rng.integers(-3, 4, size=(4, 6)).astype(np.float64)
+    ref = np.zeros((5, 6))
+    for i in range(5):
+        for j in range(6):
+            ref[i, j] = sum(a[i, k] * b[k, j] for k in range(4))
+    np.testing.assert_array_equal(oracle.dense(a, b), ref)
+    blocks = oracle.dense(a, b, apply_silu=True, split_width=2)
+    assert len(blocks) == 3
+    for i, blk in enumerate(blocks):
+        expect = [[x / (1 + math.exp(-x)) for x in row] for row in ref[:, 2 * i:2 * i + 2]]
+        np.testing.assert_allclose(blk, expect, rtol=1e-15, atol=1e-300)

@@ -352,3 +352,9 @@ def affine_terms(seed: int, width: int):
     w = (1.0 + 0.1 * rng.standard_normal(width, dtype=np.float32)).astype(np.float32)
     b = (0.1 * rng.standard_normal(width, dtype=np.float32)).astype(np.float32)
     return w, b
+
+
+def dense_operands(seed: int, M: int, N: int, K: int):
+    """Operands of a dense product: A ~ N(0, 1) [M, K] and B ~ N(0, 1/K) [K, N], bf16 values."""
+    rng = np.random.default_rng(seed)
+    return _normal(rng, (M, K), "bf16"), _normal(rng, (K, N), "bf16", std=float(np.sqrt(1.0 / K)))
