@@ -256,7 +256,9 @@ def bench_training_shape(torch, hs, W, steps, warmup):
         "workload": inp.name,
         "total_tokens": inp.total,
         "ms_per_step": round(ms, 4),
+        "scheduler_ms": round(mean_span(evs, 0, 1), 4),
         "attn_kernel_ms": round(attn_ms, 4),
+        "epilogue_ms": round(mean_span(evs, 2, 3), 4),
         "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
         "attn_kernel_tflops": round(flop / (attn_ms * 1e-3) / 1e12, 2),
         "algorithmic_gflop": round(flop / 1e9, 3),
