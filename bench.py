@@ -340,32 +340,121 @@ def bench_layer(torch, hs, W, steps, warmup, products=0):
     }
 
 
-def cpu_baseline(inp, rows):
-    """The fp64 oracle on rows 0..rows-1 of user 0 (all heads, N = 8,192): exactly
-    those rows of the headline workload. Returns the cpu_baseline object."""
-    import numpy as np
-    import oracle
+def oracle_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        return max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(inp, rows, users):
+    """The fp64 oracle on rows 0..rows-1 of each of the first `users` users (all
+    heads, N = 8,192): exactly those rows of the headline workload. Returns the
+    cpu_baseline object."""
+    import numpy as np
+    import oracle
     L = int(inp.lengths[0])
-    sl = slice(0, rows)
+    off = inp.seq_offsets
     t0 = time.perf_counter()
-    oracle.hstu_full(inp.q[sl], inp.k[sl], inp.v[sl], inp.u[sl], inp.ts[sl], np.array([0, rows]),
-                     inp.tables.pos, inp.tables.time, norm_n=L)
+    for b in range(users):
+        sl = slice(int(off[b]), int(off[b]) + rows)
+        oracle.hstu_full(inp.q[sl], inp.k[sl], inp.v[sl], inp.u[sl], inp.ts[sl], np.array([0, rows]),
+                         inp.tables.pos, inp.tables.time, norm_n=L)
     dt = time.perf_counter() - t0
-    flop = 4 * 128 * 4 * rows * (rows + 1) // 2
+    flop = users * 4 * 128 * 4 * rows * (rows + 1) // 2
     return {
         "value": round(flop / dt / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": int(cores),
+        "cores": int(oracle_threads()),
         "kind": "oracle",
-        "sample": f"fp64 oracle, user 0 rows 0..{rows - 1} of the 8x8192 workload, 4 heads, N fixed at {L}; "
-                  f"{flop / 1e9:.2f} GFLOP in {dt:.2f} s",
+        "sample": f"fp64 oracle, rows 0..{rows - 1} of users 0..{users - 1} of the 8x8192 workload, 4 heads, "
+                  f"N fixed at {L}; {flop / 1e9:.2f} GFLOP in {dt:.2f} s",
         "seconds": round(dt, 3),
     }
+
+
+def oracle_per_config(variants):
+    """The fp64 oracle timed on the host for each measured configuration: the
+    whole configuration where that takes seconds, otherwise a stated subset
+    scaled to the whole by its share of the algorithmic FLOP (marked
+    extrapolated). gpu_speedup = oracle time of the whole configuration /
+    the GPU step time of the variant."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    out = {}
+
+    def record(names, fn, timed_gflop, full_gflop, scope):
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+        whole = dt * full_gflop / timed_gflop
+        for name in names:
+            r = {"oracle_s": round(dt, 3), "timed_gflop": round(timed_gflop, 3), "scope": scope,
+                 "oracle_s_whole_config": round(whole, 3), "extrapolated": timed_gflop != full_gflop}
+            if name in variants:
+                r["gpu_speedup"] = round(whole / (variants[name]["ms_per_step"] * 1e-3), 1)
+            out[name] = r
+        log(f"  oracle {names}: {dt:.2f} s ({scope})")
+
+    pairs_full = lambda lengths: sum(int(n) * (int(n) + 1) // 2 for n in lengths)
+    t = W.training_shape()
+    g = 4 * 128 * 4 * pairs_full(t.lengths) / 1e9
+    record(["jagged_training_shape"], lambda: oracle.hstu_full(t.q, t.k, t.v, t.u, t.ts, t.seq_offsets,
+                                                               t.tables.pos, t.tables.time), g, g, "whole")
+    ci = W.kv_cache_delta()
+    h = ci.hist
+    _, new = ci.split()
+    g = 4 * 128 * 4 * sum(int(m) * int(c) + int(m) * (int(m) + 1) // 2
+                          for c, m in zip(ci.cache_lens, ci.new_lens)) / 1e9
+    record(["kv_cache_delta"], lambda: oracle.hstu_cached(h.q[new], h.u[new], h.ts[new], h.k, h.v, h.ts,
+                                                          h.seq_offsets, ci.cache_lens, ci.new_offsets(),
+                                                          h.tables.pos, h.tables.time), g, g, "whole")
+    mc = W.mfalcon_scoring()
+    mi = mc.inputs
+    hl = [int(n) - int(c) for n, c in zip(mi.lengths, mc.num_candidates)]
+    mf_gflop = lambda pairs: 4 * 128 * 4 * sum(pairs_full([n]) + int(c) * (n + 1) for n, c in pairs) / 1e9
+    e0 = int(mi.seq_offsets[1])
+    record(["mfalcon", "mfalcon_paged_history"],
+           lambda: oracle.hstu_mfalcon(mi.q[:e0], mi.k[:e0], mi.v[:e0], mi.u[:e0], mi.ts[:e0],
+                                       mi.seq_offsets[:2], mc.num_candidates[:1], mi.tables.pos, mi.tables.time),
+           mf_gflop(zip(hl[:1], mc.num_candidates[:1])), mf_gflop(zip(hl, mc.num_candidates)),
+           "user 0 of the packed [history | candidates] batch, scaled by FLOP (the paged variant returns "
+           "the candidate rows of the same computation)")
+    li = W.full_layer()
+    off = li.seq_offsets
+    k = 1
+    while k < len(li.lengths) and off[k] < 2048:
+        k += 1
+    E, HD = li.x.shape[1], li.num_heads * li.head_dim
+    layer_gflop = lambda lengths: (2 * sum(lengths) * E * 4 * HD + 4 * li.head_dim * li.num_heads *
+                                   pairs_full(lengths) + 2 * sum(lengths) * HD * E) / 1e9
+    sub = [int(n) for n in li.lengths[:k]]
+    T = int(off[k])
+    record(["full_layer", "full_layer_own_products"],
+           lambda: oracle.hstu_layer(li.x[:T], li.w1, li.w2, li.ts[:T], off[:k + 1], li.num_heads, li.head_dim,
+                                     li.tables.pos, li.tables.time),
+           layer_gflop(sub), layer_gflop([int(n) for n in li.lengths]),
+           f"users 0..{k - 1} ({T} tokens) of the 16-user layer, scaled by FLOP")
+    bt = W.training_shape()
+    dy = W.upstream_grad(81, bt.u.shape)
+    w, b = W.affine_terms(82, 4 * 128)
+    g = 5 * 2 * 128 * 4 * pairs_full(bt.lengths) / 1e9
+    record(["backward_training_shape"],
+           lambda: oracle.hstu_full_bwd(bt.q, bt.k, bt.v, bt.u, bt.ts, bt.seq_offsets, dy, bt.tables.pos,
+                                        bt.tables.time, gamma=w, beta=b), g, g,
+           "whole (forward and backward of the fp64 oracle)")
+    lq = W.long_seq()
+    n = 1024
+    dyl = W.upstream_grad(81, lq.u.shape)
+    wl, bl = W.affine_terms(82, 4 * 128)
+    record(["backward_causal_B8_L8192"],
+           lambda: oracle.hstu_full_bwd(lq.q[:n], lq.k[:n], lq.v[:n], lq.u[:n], lq.ts[:n], np.array([0, n]),
+                                        dyl[:n], lq.tables.pos, lq.tables.time, gamma=wl, beta=bl),
+           5 * 2 * 128 * 4 * pairs_full([n]) / 1e9, 5 * 2 * 128 * 4 * pairs_full(lq.lengths) / 1e9,
+           f"the first {n} tokens of user 0 as one sequence, scaled by the pair count")
+    return {"cores": int(oracle_threads()), "configs": out}
 
 
 def main():
@@ -377,6 +466,7 @@ def main():
     ap.add_argument("--variants", default="", help="comma-separated subset of the variants to run (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=8192)
+    ap.add_argument("--cpu-sample-users", type=int, default=3)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB; used to scale "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
@@ -467,9 +557,12 @@ def main():
             log(f"  {variants[name]}")
         result["variants"] = variants
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {args.cpu_sample_rows} rows")
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_rows)
+        log(f"cpu baseline: oracle on {args.cpu_sample_rows} rows of {args.cpu_sample_users} users")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_rows, args.cpu_sample_users)
         log(f"  {result['cpu_baseline']}")
+        if not args.no_variants:
+            log("oracle per configuration")
+            result["oracle_per_config"] = oracle_per_config(result.get("variants", {}))
     print(json.dumps(result), flush=True)
 
 
