@@ -151,6 +151,7 @@ def bench_cached(torch, hs, W, steps, warmup):
     kv_bytes = int(np.sum(ci.cache_lens + ci.new_lens)) * 4 * 128 * 2 * 2
     attn_ms = mean_span(evs, 1, 2)
     append_ms = mean_span(evs, 4, 0)
+    append_bytes = len(new) * 4 * 128 * 2 * 2 * 2 + len(new) * 8 * 2   # K and V read and written, ts
     return {
         "workload": ci.name,
         "ms_per_step": round(ms, 4),
@@ -161,6 +162,8 @@ def bench_cached(torch, hs, W, steps, warmup):
         "attn_kernel_kv_gbs": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1),
         "kv_bytes": kv_bytes,
         "append_ms": round(append_ms, 4),
+        "append_gbs": round(append_bytes / (append_ms * 1e-3) / 1e9, 1),
+        "append_bytes": append_bytes,
         "epilogue_ms": round(mean_span(evs, 2, 3), 4),
         "scheduler_ms": round(mean_span(evs, 0, 1), 4),
         "algorithmic_gflop": round(flop / 1e9, 3),
