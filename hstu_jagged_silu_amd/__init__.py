@@ -243,6 +243,21 @@ def _workspace(ws, nbytes, device):
     return ws
 
 
+# Debug mode (HSTU_DEBUG=1 in the environment): content-check result word in
+# the workspace header and its bits (include/hstu.h).
+HSTU_WS_DEBUG_FLAG_OFFSET = 128
+(HSTU_DEBUG_BAD_OFFSETS, HSTU_DEBUG_BAD_LENGTH, HSTU_DEBUG_BAD_CANDIDATES, HSTU_DEBUG_BAD_CACHE_LEN,
+ HSTU_DEBUG_BAD_PAGE) = 1, 2, 4, 8, 16
+
+
+def debug_flag(workspace) -> int:
+    """The content-check bits the last debug-mode call wrote into `workspace`
+    (waits for the current stream first); 0 means the content was valid."""
+    torch.cuda.current_stream().synchronize()
+    w = workspace[HSTU_WS_DEBUG_FLAG_OFFSET:HSTU_WS_DEBUG_FLAG_OFFSET + 4].cpu()
+    return int(w.view(torch.int32)[0])
+
+
 def _jagged_checks(params, q, k, v, u, ts, seq_offsets):
     H, d = params.num_heads, params.head_dim
     for name, t in (("q", q), ("k", k), ("v", v)):

@@ -1,6 +1,7 @@
 // C ABI of the HSTU attention library: host-side argument checks, workspace
 // layout and the launch sequence of each entry point. No allocation, no host
 // synchronisation; everything is queued on the caller's stream.
+#include <cstdlib>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -158,6 +159,37 @@ LnArgs ln_args(const hstu_params_t* p, const WsLayout& w, void* ws, const void* 
   return l;
 }
 
+static_assert(DBG_FLAG_OFFSET == HSTU_WS_DEBUG_FLAG_OFFSET && DBG_FLAG_OFFSET + 4 <= ALIGN,
+              "debug word inside the workspace header, after the item count");
+static_assert(DBG_BAD_OFFSETS == HSTU_DEBUG_BAD_OFFSETS && DBG_BAD_LENGTH == HSTU_DEBUG_BAD_LENGTH &&
+                  DBG_BAD_CANDIDATES == HSTU_DEBUG_BAD_CANDIDATES && DBG_BAD_CACHE_LEN == HSTU_DEBUG_BAD_CACHE_LEN &&
+                  DBG_BAD_PAGE == HSTU_DEBUG_BAD_PAGE,
+              "debug bits as declared in hstu.h");
+
+// Debug mode (HSTU_DEBUG=1 in the environment, read at every call).
+bool debug_mode() {
+  const char* e = std::getenv("HSTU_DEBUG");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+// Debug mode: check the device-side index content first; the scheduler then
+// reads the result and publishes no work when anything is wrong.
+bool debug_check(ValidateArgs v, void* ws, SchedArgs& s, hipStream_t stream) {
+  if (!debug_mode()) return true;
+  v.flag = (int32_t*)((char*)ws + DBG_FLAG_OFFSET);
+  s.debug_flag = v.flag;
+  return launch_validate(v, stream) == hipSuccess;
+}
+
+ValidateArgs rows_check(int32_t B, const int32_t* offsets, int64_t total, int32_t max_len) {
+  ValidateArgs v = {};
+  v.B = B;
+  v.offsets = offsets;
+  v.total = total;
+  v.max_len = max_len;
+  return v;
+}
+
 hstu_status_t run_attention(const hstu_params_t* p, const SchedArgs& s, const AttnArgs& a, int mode,
                             const LnArgs& l, hipStream_t stream) {
   auto mark = [&](int i) {
@@ -233,6 +265,7 @@ hstu_status_t hstu_attn_fwd(const hstu_params_t* params, int32_t batch, const in
   a.ts = ts;
   a.offsets = seq_offsets;
   LnArgs l = ln_args(params, w, ws, u, y, total_tokens);
+  if (!debug_check(rows_check(batch, seq_offsets, total_tokens, max_len), ws, s, stream)) return HSTU_ERR_LAUNCH;
   return run_attention(params, s, a, MODE_FULL, l, stream);
 }
 
@@ -275,6 +308,8 @@ hstu_status_t hstu_attn_bwd(const hstu_params_t* params, int32_t batch, const in
   a.v = v;
   a.ts = ts;
   a.offsets = seq_offsets;
+  if (!empty && !debug_check(rows_check(batch, seq_offsets, total_tokens, max_len), ws, s, stream))
+    return HSTU_ERR_LAUNCH;
   if (!mark(0)) return HSTU_ERR_LAUNCH;
   if (!empty) {
     if (launch_sched(s, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
@@ -373,6 +408,9 @@ hstu_status_t hstu_mfalcon_fwd(const hstu_params_t* params, int32_t batch, const
   a.offsets = seq_offsets;
   a.num_cand = num_candidates;
   LnArgs l = ln_args(params, w, ws, u, y, total_tokens);
+  ValidateArgs chk = rows_check(batch, seq_offsets, total_tokens, max_len);
+  chk.num_cand = num_candidates;
+  if (!debug_check(chk, ws, s, stream)) return HSTU_ERR_LAUNCH;
   return run_attention(params, s, a, MODE_MFALCON, l, stream);
 }
 
@@ -458,6 +496,14 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_params_t* params, int32_t batch, c
   l.B = batch;
   l.offsets = new_offsets;
   l.cache_lens = cache_lens;
+  ValidateArgs chk = rows_check(batch, new_offsets, total_new, max_new);
+  chk.cache_lens = cache_lens;
+  chk.max_keys = max_total;
+  chk.keys_add_rows = 1;
+  chk.page_table = cache->page_table;
+  chk.num_pages = cache->num_pages;
+  chk.max_pages = cache->max_pages_per_seq;
+  if (!debug_check(chk, ws, s, stream)) return HSTU_ERR_LAUNCH;
   return run_attention(params, s, a, MODE_CACHED, l, stream);
 }
 
@@ -509,6 +555,13 @@ hstu_status_t hstu_mfalcon_fwd_cached(const hstu_params_t* params, int32_t batch
   l.B = batch;
   l.offsets = cand_offsets;
   l.cache_lens = hist_lens;
+  ValidateArgs chk = rows_check(batch, cand_offsets, total_cand, max_cand);
+  chk.cache_lens = hist_lens;
+  chk.max_keys = max_hist;
+  chk.page_table = cache->page_table;
+  chk.num_pages = cache->num_pages;
+  chk.max_pages = cache->max_pages_per_seq;
+  if (!debug_check(chk, ws, s, stream)) return HSTU_ERR_LAUNCH;
   return run_attention(params, s, a, MODE_MFALCON_PAGED, l, stream);
 }
 

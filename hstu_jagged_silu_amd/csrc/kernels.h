@@ -48,6 +48,7 @@ struct SchedArgs {
   const int32_t* num_cand;       // M-FALCON
   int32_t chunk_keys;            // key split (cached path), multiple of KT
   int32_t cost_shift;            // cost bin = min(cost >> shift, NBINS - 1)
+  const int32_t* debug_flag;     // debug mode: nonzero content-check bits -> empty work list
   int64_t max_items;
   int32_t* prefix;               // [B+1] scratch
   WorkItem* items;
@@ -80,6 +81,31 @@ struct LnArgs {
   int32_t B;
   const int32_t* offsets;
   const int32_t* cache_lens;
+};
+
+// Debug-mode content checks (HSTU_DEBUG=1): bits written to the workspace
+// header word at DBG_FLAG_OFFSET (0 when the content is valid).
+constexpr int DBG_FLAG_OFFSET = 128;
+enum DebugBits : int32_t {
+  DBG_BAD_OFFSETS = 1,     // offsets[0] != 0, a decreasing pair, or offsets[B] != total rows
+  DBG_BAD_LENGTH = 2,      // a length above max_len
+  DBG_BAD_CANDIDATES = 4,  // num_candidates[b] outside [0, L_b]
+  DBG_BAD_CACHE_LEN = 8,   // a cache (history) length below 0 or keys above their bound
+  DBG_BAD_PAGE = 16,       // a needed page missing from the table or outside the pool
+};
+struct ValidateArgs {
+  int32_t B;
+  const int32_t* offsets;        // [B+1] rows of this call
+  int64_t total;                 // expected offsets[B]
+  int32_t max_len;               // bound on every length
+  const int32_t* num_cand;       // M-FALCON counts, or null
+  const int32_t* cache_lens;     // cache (history) lengths, or null
+  int64_t max_keys;              // bound on the keys per user
+  int32_t keys_add_rows;         // keys = cache_len + L (cached, append) or cache_len (paged M-FALCON)
+  int32_t first_pos_is_cache;    // pages checked from position cache_len (append) or 0 (forward)
+  const int32_t* page_table;     // [B, max_pages], or null
+  int32_t num_pages, max_pages;
+  int32_t* flag;                 // result word
 };
 
 struct AppendArgs {
@@ -162,6 +188,7 @@ struct LnBwdArgs {
 };
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s);  // scheduler + key timestamp ranges
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int mode, int64_t grid, hipStream_t s);
 hipError_t launch_ln_gate(const LnArgs& a, int dtype, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);

@@ -168,6 +168,15 @@ __device__ void key_time_ranges(const SchedArgs& a) {
 }
 
 __global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(SchedArgs a) {
+  if (a.debug_flag && *a.debug_flag != 0) {
+    // debug mode, bad index content: an empty work list (and empty per-user
+    // counts for the reductions that read them)
+    if (blockIdx.x == 0) {
+      for (int i = threadIdx.x; i <= a.B; i += SCHED_THREADS) a.prefix[i] = 0;
+      if (threadIdx.x == 0) *a.count = 0;
+    }
+    return;
+  }
   if (blockIdx.x > 0) {
     key_time_ranges(a);
     return;

@@ -43,8 +43,17 @@
  *     return a status; nothing is launched then. HSTU_ERR_LAUNCH reports a
  *     failed kernel launch. Device-side content (offsets, lengths, page
  *     indices, timestamps) is trusted: page indices outside [0, num_pages)
- *     read as zero keys and are never written, rows beyond T are never read,
- *     but inconsistent offsets give unspecified values in Y.
+ *     read as zero keys and are never written, but inconsistent offsets or
+ *     lengths are undefined behaviour.
+ *   - Debug mode: with HSTU_DEBUG=1 in the environment (read at every call),
+ *     hstu_attn_fwd, hstu_attn_fwd_cached, hstu_mfalcon_fwd,
+ *     hstu_mfalcon_fwd_cached and hstu_attn_bwd first check that content on
+ *     the device and write the result, an int32 of hstu_debug_bits_t, at byte
+ *     HSTU_WS_DEBUG_FLAG_OFFSET of the workspace (0: valid). When it is not 0
+ *     no attention work runs (Y, or the gradients, then hold unspecified but
+ *     finite-sized garbage, and no memory outside the given buffers is read
+ *     or written). The call stays asynchronous: read the word after the
+ *     stream has finished. hstu_layer_fwd checks through its attention call.
  *   - Timestamps are int64 seconds. Within one user any two timestamps must
  *     differ by less than 2^62.
  */
@@ -69,6 +78,17 @@ typedef enum {
 } hstu_status_t;
 
 typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype_t;
+
+/* Debug mode (HSTU_DEBUG=1): where the content-check result sits in the
+ * workspace, and its bits. */
+#define HSTU_WS_DEBUG_FLAG_OFFSET 128
+typedef enum {
+  HSTU_DEBUG_BAD_OFFSETS = 1,     /* offsets[0] != 0, decreasing, or offsets[B] != total rows */
+  HSTU_DEBUG_BAD_LENGTH = 2,      /* a user's rows above max_len (max_new, max_cand)           */
+  HSTU_DEBUG_BAD_CANDIDATES = 4,  /* num_candidates[b] outside [0, L_b]                        */
+  HSTU_DEBUG_BAD_CACHE_LEN = 8,   /* cache (history) length < 0 or keys above max_total       */
+  HSTU_DEBUG_BAD_PAGE = 16        /* a needed page missing from the table or not in the pool  */
+} hstu_debug_bits_t;
 
 /* Which entry point a workspace is sized for. */
 typedef enum {

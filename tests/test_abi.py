@@ -282,3 +282,13 @@ def test_pair_count_matches_closed_forms():
     assert hs.pair_count("full", [8192] * 8) == 8 * 8192 * 8193 // 2
     assert hs.pair_count("cached", [128] * 8, [8192] * 8) == 8 * (128 * 8192 + 128 * 129 // 2)
     assert hs.pair_count("mfalcon", [4096] * 4, [1024] * 4) == 4 * (4096 * 4097 // 2 + 1024 * 4097)
+
+
+def test_debug_mode_constants_match_header():
+    import re
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "hstu.h")).read()
+    assert int(re.search(r"#define HSTU_WS_DEBUG_FLAG_OFFSET (\d+)", hdr).group(1)) == hs.HSTU_WS_DEBUG_FLAG_OFFSET
+    for name in ("OFFSETS", "LENGTH", "CANDIDATES", "CACHE_LEN", "PAGE"):
+        val = int(re.search(rf"HSTU_DEBUG_BAD_{name} = (\d+)", hdr).group(1))
+        assert val == getattr(hs, f"HSTU_DEBUG_BAD_{name}"), name
+    assert hs.HSTU_WS_DEBUG_FLAG_OFFSET + 4 <= 256   # inside the 256-byte header, after the item count
