@@ -69,6 +69,15 @@ def test_ragged_lengths_all_gradients(d):
     check(g, ref, label=f"ragged d={d}")
 
 
+def test_largest_position_table():
+    # the backward's largest position table (512 buckets), users longer than it
+    inp = W.jagged("bwd_maxpos", 66, [700, 300], 2, 64, "bf16", 512, 64)
+    inp.tables.pos *= 25.0
+    dy = W.upstream_grad(67, inp.u.shape)
+    g, ref = run_bwd(inp, dy, affine=W.affine_terms(68, 2 * 64))
+    check(g, ref, label="512 position buckets")
+
+
 def test_per_head_tables_alpha_norm_no_affine():
     inp = W.jagged("bwd_opts", 64, [300, 45, 190], 4, 128, "bf16", 64, 40)
     dy = W.upstream_grad(65, inp.u.shape)

@@ -83,6 +83,23 @@ def test_unordered_and_huge_timestamps():
     check(run_full(inp), oracle_full(inp), "bf16", "huge ts")
 
 
+def test_maximum_sizes_sampled_rows():
+    """The largest supported shapes: H*d = 2,048 (16 heads of 128), a 2,048-entry
+    position table, 64 time buckets, users longer than the position table."""
+    inp = W.jagged("max", 99, [3000, 2500, 40], 16, 128, "bf16", 2048, 64)
+    inp.tables.pos *= 25.0   # large enough to move the outputs (the draws have variance 0.02)
+    y = to_np(run_full(inp))
+    rng = np.random.default_rng(10)
+    rows = np.unique(np.concatenate([[0, 2046, 2047, 2048, 2999, 3000, 5047, 5048, 5499, 5500, 5539],
+                                     rng.integers(0, inp.total, size=30)]))
+    y_ref = oracle.hstu_full_rows(rows, inp.q, inp.k, inp.v, inp.u, inp.ts, inp.seq_offsets, inp.tables.pos,
+                                  inp.tables.time)
+    err = oracle.max_rel_row_error(y[rows], y_ref)
+    print(f"maximum sizes sampled rows max row rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    assert np.isfinite(y).all()
+
+
 def test_long_sequences_sampled_rows():
     """8 users x 8,192 tokens, 4 x 128, bf16 (the benchmark's workload): sampled rows."""
     inp = W.long_seq()
