@@ -19,7 +19,11 @@
 namespace hstu {
 
 constexpr int SCHED_THREADS = 1024;
+constexpr int SCHED_WAVES = SCHED_THREADS / 64;
 constexpr int NBINS = 1024;
+// Batches of at most this many users keep the per-user table and the item
+// prefix in LDS; larger ones read them from global memory.
+constexpr int LDS_USERS = 2048;
 
 struct UserGeo {
   int nq_causal;   // causal query tiles
@@ -27,14 +31,27 @@ struct UserGeo {
   int L, C, n;     // rows, cached prefix, history length
 };
 
-__device__ inline UserGeo user_geo(const SchedArgs& a, int b) {
+// What the work list needs to know of one user: its query rows, and its
+// cached prefix (paged modes) or candidate count (M-FALCON).
+struct UserRaw {
+  int L, X;
+};
+
+__device__ inline UserRaw user_raw(const SchedArgs& a, int b) {
+  UserRaw r;
+  r.L = max(0, a.offsets[b + 1] - a.offsets[b]);
+  r.X = mode_paged(a.mode) ? a.cache_lens[b] : (a.mode == MODE_MFALCON ? a.num_cand[b] : 0);
+  return r;
+}
+
+__device__ inline UserGeo user_geo(const SchedArgs& a, UserRaw r) {
   UserGeo g;
-  g.L = max(0, a.offsets[b + 1] - a.offsets[b]);
-  g.C = mode_paged(a.mode) ? a.cache_lens[b] : 0;
+  g.L = r.L;
+  g.C = mode_paged(a.mode) ? r.X : 0;
   g.n = g.L;
   g.nq_cand = 0;
   if (a.mode == MODE_MFALCON) {
-    const int m = min(max(a.num_cand[b], 0), g.L);
+    const int m = min(max(r.X, 0), g.L);
     g.n = g.L - m;
     g.nq_cand = (int)ceil_div(m, QT);
   }
@@ -69,8 +86,8 @@ __device__ inline int user_items_per_head(const SchedArgs& a, const UserGeo& g) 
 }
 
 // the local-th item of user b
-__device__ inline WorkItem make_item(const SchedArgs& a, int b, int local) {
-  const UserGeo g = user_geo(a, b);
+__device__ inline WorkItem make_item(const SchedArgs& a, int b, UserRaw r, int local) {
+  const UserGeo g = user_geo(a, r);
   const int per_head = user_items_per_head(a, g);
   WorkItem w;
   w.b = b;
@@ -117,20 +134,28 @@ __device__ inline int item_bin(const SchedArgs& a, const WorkItem& w) {
   return min(cost >> a.cost_shift, NBINS - 1);
 }
 
-// block-wide exclusive scan of one value per thread; returns the block total
-__device__ inline int block_scan(int x, int* tmp, int& excl) {
-  const int tid = threadIdx.x;
-  tmp[tid] = x;
-  __syncthreads();
-  for (int off = 1; off < SCHED_THREADS; off <<= 1) {
-    const int y = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += y;
-    __syncthreads();
+// Block-wide exclusive scan of one value per thread; returns the block
+// total. Shuffle scan inside each wave, then every thread adds the totals of
+// the waves before its own: two barriers in all.
+__device__ inline int block_scan(int x, int* wsum, int& excl) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = x;
+  #pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
   }
-  excl = tmp[tid] - x;
-  const int total = tmp[SCHED_THREADS - 1];
+  if (lane == 63) wsum[wave] = inc;
   __syncthreads();
+  int before = 0, total = 0;
+  #pragma unroll
+  for (int w = 0; w < SCHED_WAVES; ++w) {
+    const int t = wsum[w];
+    before += w < wave ? t : 0;
+    total += t;
+  }
+  excl = before + inc - x;
+  __syncthreads();  // wsum is reused by the next scan
   return total;
 }
 
@@ -181,66 +206,70 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(SchedArgs a) {
     key_time_ranges(a);
     return;
   }
-  __shared__ int tmp[SCHED_THREADS];
+  __shared__ int wsum[SCHED_WAVES];
   __shared__ int hist[NBINS];
   __shared__ int start[NBINS];
+  __shared__ int s_pref[LDS_USERS + 1];
+  __shared__ UserRaw s_raw[LDS_USERS];
   const int tid = threadIdx.x;
+  const bool in_lds = a.B <= LDS_USERS;
+  for (int i = tid; i < NBINS; i += SCHED_THREADS) hist[i] = 0;
 
   // 1. items per user -> exclusive prefix over users
   int carry = 0;
   for (int base = 0; base < a.B; base += SCHED_THREADS) {
     const int b = base + tid;
     int c = 0;
-    if (b < a.B) c = a.H * user_items_per_head(a, user_geo(a, b));
+    if (b < a.B) {
+      const UserRaw r = user_raw(a, b);
+      if (in_lds) s_raw[b] = r;
+      c = a.H * user_items_per_head(a, user_geo(a, r));
+    }
     int excl;
-    const int tot = block_scan(c, tmp, excl);
-    if (b < a.B) a.prefix[b] = carry + excl;
+    const int tot = block_scan(c, wsum, excl);
+    if (b < a.B) {
+      a.prefix[b] = carry + excl;
+      if (in_lds) s_pref[b] = carry + excl;
+    }
     carry += tot;
   }
   int total = carry;
   if ((int64_t)total > a.max_items) total = (int)a.max_items;  // cannot happen with a valid bound
-  if (tid == 0) a.prefix[a.B] = carry;
-  for (int i = tid; i < NBINS; i += SCHED_THREADS) hist[i] = 0;
+  if (tid == 0) {
+    a.prefix[a.B] = carry;
+    if (in_lds) s_pref[a.B] = carry;
+  }
   __threadfence_block();
   __syncthreads();
 
-  auto user_of = [&](int g) {
+  auto pref = [&](int i) { return in_lds ? s_pref[i] : a.prefix[i]; };
+  auto raw = [&](int b) { return in_lds ? s_raw[b] : user_raw(a, b); };
+  auto item = [&](int g) {
     int lo = 0, hi = a.B - 1;  // largest b with prefix[b] <= g
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (a.prefix[mid] <= g) lo = mid; else hi = mid - 1;
+      if (pref(mid) <= g) lo = mid; else hi = mid - 1;
     }
-    return lo;
+    return make_item(a, lo, raw(lo), g - pref(lo));
   };
 
   // 2. cost histogram
-  for (int g = tid; g < total; g += SCHED_THREADS) {
-    const int b = user_of(g);
-    const WorkItem w = make_item(a, b, g - a.prefix[b]);
-    atomicAdd(&hist[item_bin(a, w)], 1);
-  }
+  for (int g = tid; g < total; g += SCHED_THREADS) atomicAdd(&hist[item_bin(a, item(g))], 1);
   __syncthreads();
 
-  // 3. start of each bin, most expensive bin first
+  // 3. start of each bin, most expensive bin first (one bin per thread)
   {
-    const int per = NBINS / SCHED_THREADS;  // bins per thread (1)
-    int s = 0;
-    for (int i = 0; i < per; ++i) s += hist[NBINS - 1 - (tid * per + i)];
+    static_assert(NBINS == SCHED_THREADS, "one cost bin per thread");
+    const int bin = NBINS - 1 - tid;
     int excl;
-    block_scan(s, tmp, excl);
-    int acc = excl;
-    for (int i = 0; i < per; ++i) {
-      const int bin = NBINS - 1 - (tid * per + i);
-      start[bin] = acc;
-      acc += hist[bin];
-    }
+    block_scan(hist[bin], wsum, excl);
+    start[bin] = excl;
   }
   __syncthreads();
 
   // 4. scatter
   for (int g = tid; g < total; g += SCHED_THREADS) {
-    const int b = user_of(g);
-    const WorkItem w = make_item(a, b, g - a.prefix[b]);
+    const WorkItem w = item(g);
     const int pos = atomicAdd(&start[item_bin(a, w)], 1);
     a.items[pos] = w;
   }
