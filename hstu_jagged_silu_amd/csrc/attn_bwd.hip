@@ -49,6 +49,17 @@ struct BwdTables {
   float time_t[64];           // -log2(e) * time table, indexed by clz64(|dt| + 1)
 };
 
+// Adds v to a float in LDS (ds_add_f32, no return value). The compiler's own
+// form of this atomic first waits for every LDS DMA in flight, since it does
+// not separate the histogram from the DMA targets, and that would drain the
+// next tile's prefetch at every run flush. The barrier that ends each tile
+// waits for the add (lgkmcnt(0)); a later read by the same wave is ordered
+// behind it because LDS serves a wave's requests in order.
+__device__ inline void lds_add_f32(float* p, float v) {
+  const uint32_t addr = (uint32_t)(uintptr_t)LDS_PTR(float, p);
+  asm volatile("ds_add_f32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
 // One histogram per wave (no two waves add to the same word, so every sum
 // runs in program order and the result does not depend on wave timing).
 struct RabHist {
@@ -342,7 +353,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
             if (ok && row_ok) {
               if (a.pos_tab) {
                 if (pb != cur_p) {
-                  if (cur_p >= 0) atomicAdd(&hist.pos[wave][cur_p], run_p);
+                  if (cur_p >= 0) lds_add_f32(&hist.pos[wave][cur_p], run_p);
                   cur_p = pb;
                   run_p = 0.0f;
                 }
@@ -350,7 +361,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
               }
               if (has_time) {
                 if (tb != cur_t) {
-                  if (cur_t >= 0) atomicAdd(&hist.time[wave][cur_t], run_t);
+                  if (cur_t >= 0) lds_add_f32(&hist.time[wave][cur_t], run_t);
                   cur_t = tb;
                   run_t = 0.0f;
                 }
@@ -375,8 +386,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
-    if (cur_p >= 0) atomicAdd(&hist.pos[wave][cur_p], run_p);
-    if (cur_t >= 0) atomicAdd(&hist.time[wave][cur_t], run_t);
+    if (cur_p >= 0) lds_add_f32(&hist.pos[wave][cur_p], run_p);
+    if (cur_t >= 0) lds_add_f32(&hist.time[wave][cur_t], run_t);
     if (fast) {
       // rows past q_len have zero dO, so their dS' is 0 and they add nothing
       const float tot = wave_sum_f(tile_sum);
@@ -548,17 +559,38 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
     #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       if (j0 + 32 * qb + 31 < w_kmin) continue;
+      // One wave per SIMD leaves nothing to hide LDS latency behind, and
+      // registers to spare: every operand read of the step is issued before
+      // the MFMA that needs the first one, the two chains interleave, and the
+      // transposed operands of dV and dK are read while the SiLU runs.
+      bf16x8 qa[G::NQOP], ga[G::NQOP];
+      #pragma unroll
+      for (int i = 0; i < G::NQOP; ++i) {
+        qa[i] = *(__attribute__((address_space(3))) const bf16x8*)(ql + qoff[i] + qb * 32 * G::ROWB);
+        ga[i] = *(__attribute__((address_space(3))) const bf16x8*)(gl + qoff[i] + qb * 32 * G::ROWB);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 s = f32x16{}, dp = f32x16{};
       #pragma unroll
       for (int i = 0; i < G::NQOP; ++i) {
-        const bf16x8 qa = *(__attribute__((address_space(3))) const bf16x8*)(ql + qoff[i] + qb * 32 * G::ROWB);
-        s = M::run(qa, kop[i], s);
+        s = M::run(qa[i], kop[i], s);
+        dp = M::run(ga[i], vop[i], dp);
       }
+      bf16x8 gt[G::NDB][2], qt[G::NDB][2];
       #pragma unroll
-      for (int i = 0; i < G::NQOP; ++i) {
-        const bf16x8 ga = *(__attribute__((address_space(3))) const bf16x8*)(gl + qoff[i] + qb * 32 * G::ROWB);
-        dp = M::run(ga, vop[i], dp);
+      for (int db = 0; db < G::NDB; ++db) {
+        #pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const int o = (2 * qb + cc) * 16 * G::ROWB;
+          const v4i16 glo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(gl + qtr[db][0] + o));
+          const v4i16 ghi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(gl + qtr[db][1] + o));
+          gt[db][cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7));
+          const v4i16 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(ql + qtr[db][0] + o));
+          const v4i16 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(ql + qtr[db][1] + o));
+          qt[db][cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
       bf16x8 pb[2], dsb[2];
       if (fast) {
         #pragma unroll
@@ -569,21 +601,34 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
           dsb[v >> 3][v & 7] = (bf16)ds;
         }
       } else {
+        // bias of the 16 pairs first (table reads in one batch per table),
+        // then the SiLU terms
         auto general = [&](auto small_tag) {
           constexpr bool SMALL = decltype(small_tag)::value;
+          float cb[16];
+          if (a.pos_tab) {
+            #pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int rel = j0 + M::key_of(qb, v, hl) - kpos;
+              cb[v] = tab.pos_t[min((unsigned)rel, (unsigned)(n_pos - 1))];
+            }
+          } else {
+            #pragma unroll
+            for (int v = 0; v < 16; ++v) cb[v] = 0.0f;
+          }
+          if (has_time) {
+            #pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int qv = M::key_of(qb, v, 0);
+              cb[v] += tab.time_t[time_z<SMALL>(SMALL ? 0 : ts_l[qv], tsk, SMALL ? tsl_lo[qv] : 0, tsk_lo)];
+            }
+          }
           #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int ql_ = M::key_of(qb, v, hl);  // query row within the tile
-            const int qpos = j0 + ql_;
+            const int qpos = j0 + M::key_of(qb, v, hl);  // query row
             const bool ok = key_ok && qpos >= kpos && qpos < L;
-            const int rel = qpos - kpos;
-            float cb = a.pos_tab ? tab.pos_t[min((unsigned)rel, (unsigned)(n_pos - 1))] : 0.0f;
-            if (has_time) {
-              const int qv = M::key_of(qb, v, 0);
-              cb += tab.time_t[time_z<SMALL>(SMALL ? 0 : ts_l[qv], tsk, SMALL ? tsl_lo[qv] : 0, tsk_lo)];
-            }
             float p, ds;
-            silu_fwd_bwd(ok ? fmaf(s[v], sc, cb) : MASKED_Y, dp[v], p, ds);
+            silu_fwd_bwd(ok ? fmaf(s[v], sc, cb[v]) : MASKED_Y, dp[v], p, ds);
             pb[v >> 3][v & 7] = (bf16)p;
             dsb[v >> 3][v & 7] = (bf16)ds;
           }
@@ -596,15 +641,8 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
       for (int db = 0; db < G::NDB; ++db) {
         #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          const int o = (2 * qb + cc) * 16 * G::ROWB;
-          const v4i16 glo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(gl + qtr[db][0] + o));
-          const v4i16 ghi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(gl + qtr[db][1] + o));
-          const bf16x8 gt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7));
-          dvacc[db] = M::run(gt, pb[cc], dvacc[db]);
-          const v4i16 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(ql + qtr[db][0] + o));
-          const v4i16 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(ql + qtr[db][1] + o));
-          const bf16x8 qt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
-          dkacc[db] = M::run(qt, dsb[cc], dkacc[db]);
+          dvacc[db] = M::run(gt[db][cc], pb[cc], dvacc[db]);
+          dkacc[db] = M::run(qt[db][cc], dsb[cc], dkacc[db]);
         }
       }
     }
