@@ -61,7 +61,7 @@ def check(g, ref, tol=TOL["bf16"], label=""):
         assert v <= tol, (k, v)
 
 
-@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("d", [128, 64, 32])
 def test_ragged_lengths_all_gradients(d):
     inp = W.jagged(f"bwd_ragged_d{d}", 61, [1, 77, 200, 130, 0, 64, 129], 2, d, "bf16", 128, 128)
     dy = W.upstream_grad(62, inp.u.shape)
