@@ -253,8 +253,23 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(SchedArgs a) {
     return make_item(a, lo, raw(lo), g - pref(lo));
   };
 
-  // 2. cost histogram
-  for (int g = tid; g < total; g += SCHED_THREADS) atomicAdd(&hist[item_bin(a, item(g))], 1);
+  // 2. cost histogram. A thread's first KEEP items stay in registers for the
+  // scatter (lists of up to KEEP * 1024 items are built once); later ones
+  // are rebuilt there.
+  constexpr int KEEP = 4;
+  WorkItem kept[KEEP];
+  int kept_bin[KEEP];
+  #pragma unroll
+  for (int k = 0; k < KEEP; ++k) {
+    const int g = tid + k * SCHED_THREADS;
+    kept_bin[k] = -1;
+    if (g < total) {
+      kept[k] = item(g);
+      kept_bin[k] = item_bin(a, kept[k]);
+      atomicAdd(&hist[kept_bin[k]], 1);
+    }
+  }
+  for (int g = tid + KEEP * SCHED_THREADS; g < total; g += SCHED_THREADS) atomicAdd(&hist[item_bin(a, item(g))], 1);
   __syncthreads();
 
   // 3. start of each bin, most expensive bin first (one bin per thread)
@@ -268,7 +283,11 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(SchedArgs a) {
   __syncthreads();
 
   // 4. scatter
-  for (int g = tid; g < total; g += SCHED_THREADS) {
+  #pragma unroll
+  for (int k = 0; k < KEEP; ++k) {
+    if (kept_bin[k] >= 0) a.items[atomicAdd(&start[kept_bin[k]], 1)] = kept[k];
+  }
+  for (int g = tid + KEEP * SCHED_THREADS; g < total; g += SCHED_THREADS) {
     const WorkItem w = item(g);
     const int pos = atomicAdd(&start[item_bin(a, w)], 1);
     a.items[pos] = w;
