@@ -49,24 +49,6 @@ __global__ __launch_bounds__(64 * LN_ROWS) void ln_gate_kernel(LnArgs a) {
   if (row >= a.T) return;
   const int nch = a.HD / 4;
 
-  // number of key splits that wrote this row (cached path)
-  int nsplit = 1;
-  if (a.chunk_keys > 0) {
-    int lo = 0, hi = a.B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.offsets[mid] <= row) lo = mid; else hi = mid - 1;
-    }
-    const int b = lo;
-    const int m = (int)(row - a.offsets[b]);
-    const int Lb = a.offsets[b + 1] - a.offsets[b];
-    // keys seen by the work item that holds this row: causal new tokens end at
-    // their tile's last row; paged candidates see the whole history
-    const int kend = a.mode == MODE_MFALCON_PAGED ? a.cache_lens[b]
-                                                  : a.cache_lens[b] + min((m / QT + 1) * QT, Lb);
-    nsplit = max(1, min((int)ceil_div(kend, a.chunk_keys), a.n_chunks));
-  }
-
   bool on[NCH];
   int col[NCH];
   #pragma unroll
@@ -75,6 +57,7 @@ __global__ __launch_bounds__(64 * LN_ROWS) void ln_gate_kernel(LnArgs a) {
     on[i] = FULL_LANES || c < nch;
     col[i] = 4 * (FULL_LANES ? c : min(c, nch - 1));
   }
+  // the row's own loads first: they do not depend on the split count
   const float* orow = a.o + row * a.HD;
   const T* urow = (const T*)a.u + row * a.HD;
   f32x4 z[NCH], u[NCH];
@@ -82,7 +65,58 @@ __global__ __launch_bounds__(64 * LN_ROWS) void ln_gate_kernel(LnArgs a) {
   for (int i = 0; i < NCH; ++i) z[i] = *(const f32x4*)(orow + col[i]);
   #pragma unroll
   for (int i = 0; i < NCH; ++i) u[i] = load4(urow + col[i]);
-  for (int k = 1; k < nsplit; ++k) {
+
+  // number of key splits that wrote this row (cached path)
+  int nsplit = 1;
+  if (a.chunk_keys > 0) {
+    // the row's user b: how many of offsets[1..B] are <= row (offsets ascend
+    // and offsets[B] = T > row)
+    int b = 0, off_b, off_b1, clen;
+    if (a.B <= 64) {
+      // one wave-wide load of offsets[1..B] and cache_lens[0..B-1]
+      const int o = lane < a.B ? a.offsets[lane + 1] : INT_MAX;
+      const int c = lane < a.B ? a.cache_lens[lane] : 0;
+      b = min(__popcll(__ballot(o <= row)), a.B - 1);
+      off_b1 = __shfl(o, b);
+      const int prev = __shfl(o, max(b - 1, 0));
+      off_b = b > 0 ? prev : 0;  // offsets[0] = 0
+      clen = __shfl(c, b);
+    } else {
+      for (int base = 0; base < a.B; base += 64) {
+        const int i = base + 1 + lane;
+        b += __popcll(__ballot(i <= a.B && a.offsets[i] <= row));
+      }
+      b = min(b, a.B - 1);
+      off_b = a.offsets[b];
+      off_b1 = a.offsets[b + 1];
+      clen = a.cache_lens[b];
+    }
+    const int m = (int)(row - off_b);
+    const int Lb = off_b1 - off_b;
+    // keys seen by the work item that holds this row: causal new tokens end at
+    // their tile's last row; paged candidates see the whole history
+    const int kend = a.mode == MODE_MFALCON_PAGED ? clen : clen + min((m / QT + 1) * QT, Lb);
+    nsplit = max(1, min((int)ceil_div(kend, a.chunk_keys), a.n_chunks));
+  }
+
+  // splits in groups whose loads are all in flight before the first add;
+  // the adds keep split order
+  constexpr int GS = NCH <= 2 ? 4 : (NCH <= 4 ? 2 : 1);
+  int k = 1;
+  for (; k + GS <= nsplit; k += GS) {
+    f32x4 t[GS][NCH];
+    #pragma unroll
+    for (int j = 0; j < GS; ++j) {
+      #pragma unroll
+      for (int i = 0; i < NCH; ++i) t[j][i] = *(const f32x4*)(orow + (k + j) * a.o_chunk_stride + col[i]);
+    }
+    #pragma unroll
+    for (int j = 0; j < GS; ++j) {
+      #pragma unroll
+      for (int i = 0; i < NCH; ++i) z[i] += t[j][i];
+    }
+  }
+  for (; k < nsplit; ++k) {
     #pragma unroll
     for (int i = 0; i < NCH; ++i) z[i] += *(const f32x4*)(orow + k * a.o_chunk_stride + col[i]);
   }
