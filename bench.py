@@ -146,6 +146,17 @@ def bench_cached(torch, hs, W, steps, warmup):
                                 timing_events=ev)
 
     ms, evs = timed(step, steps, warmup, torch, n_events=5)
+    # the same step captured once as a HIP graph and replayed: a serving loop
+    # at this size is bound by launch latency (4 kernels per step)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(None)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(None)
+    graph_ms, _ = timed(lambda ev: graph.replay(), steps, warmup, torch, n_events=0)
     pairs = 4 * hs.pair_count("cached", [int(x) for x in ci.new_lens], [int(x) for x in ci.cache_lens])
     flop = 4 * 128 * pairs
     kv_bytes = int(np.sum(ci.cache_lens + ci.new_lens)) * 4 * 128 * 2 * 2
@@ -158,6 +169,8 @@ def bench_cached(torch, hs, W, steps, warmup):
         "step": "paged append of the new tokens + cached forward (schedule, attention, split reduce + LN/gate)",
         "attn_kernel_ms": round(attn_ms, 4),
         "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+        "graph_ms_per_step": round(graph_ms, 4),
+        "graph_tflops": round(flop / (graph_ms * 1e-3) / 1e12, 2),
         "attn_kernel_tflops": round(flop / (attn_ms * 1e-3) / 1e12, 2),
         "attn_kernel_kv_gbs": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1),
         "kv_bytes": kv_bytes,
@@ -233,6 +246,8 @@ def bench_mfalcon_paged(torch, hs, W, steps, warmup):
         "ms_per_step": round(ms, 4),
         "attn_kernel_ms": round(attn_ms, 4),
         "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+        "graph_ms_per_step": round(graph_ms, 4),
+        "graph_tflops": round(flop / (graph_ms * 1e-3) / 1e12, 2),
         "attn_kernel_tflops": round(flop / (attn_ms * 1e-3) / 1e12, 2),
         "attn_kernel_kv_gbs": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1),
         "algorithmic_gflop": round(flop / 1e9, 3),
