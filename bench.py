@@ -81,6 +81,21 @@ def mean_span(evs, a, b):
     return sum(e[a].elapsed_ms(e[b]) for e in evs) / len(evs)
 
 
+def graph_replay_ms(fn, steps, warmup, torch):
+    """fn() captured once as a HIP graph (after an eager warm-up on a side
+    stream), then replayed: ms per replay."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    ms, _ = timed(lambda ev: graph.replay(), steps, warmup, torch, n_events=0)
+    return ms
+
+
 def dev(torch, x, dt=None):
     import numpy as np
     t = torch.from_numpy(np.ascontiguousarray(x))
@@ -148,15 +163,7 @@ def bench_cached(torch, hs, W, steps, warmup):
     ms, evs = timed(step, steps, warmup, torch, n_events=5)
     # the same step captured once as a HIP graph and replayed: a serving loop
     # at this size is bound by launch latency (4 kernels per step)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step(None)
-    torch.cuda.current_stream().wait_stream(side)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step(None)
-    graph_ms, _ = timed(lambda ev: graph.replay(), steps, warmup, torch, n_events=0)
+    graph_ms = graph_replay_ms(lambda: step(None), steps, warmup, torch)
     pairs = 4 * hs.pair_count("cached", [int(x) for x in ci.new_lens], [int(x) for x in ci.cache_lens])
     flop = 4 * 128 * pairs
     kv_bytes = int(np.sum(ci.cache_lens + ci.new_lens)) * 4 * 128 * 2 * 2
@@ -236,6 +243,7 @@ def bench_mfalcon_paged(torch, hs, W, steps, warmup):
     fn = lambda ev: hs.hstu_mfalcon_fwd_cached(q, k, v, u, ts, coff, hl, max_cand, max_hist, cache, p, y=y,
                                                workspace=ws, timing_events=ev)
     ms, evs = timed(fn, steps, warmup, torch)
+    graph_ms = graph_replay_ms(lambda: fn(None), steps, warmup, torch)
     # candidate pairs only: each candidate sees its user's history and itself
     pairs = 4 * sum(int(m) * (int(n) + 1) for n, m in zip(ci.hist_lens, ci.num_candidates))
     flop = 4 * 128 * pairs
@@ -268,6 +276,7 @@ def bench_training_shape(torch, hs, W, steps, warmup):
                      dtype=torch.uint8, device="cuda")
     fn = lambda ev: hs.hstu_attn_fwd(q, k, v, u, ts, off, inp.max_len, p, y=y, workspace=ws, timing_events=ev)
     ms, evs = timed(fn, steps, warmup, torch)
+    graph_ms = graph_replay_ms(lambda: fn(None), steps, warmup, torch)
     flop = 4 * 128 * 4 * hs.pair_count("full", [int(x) for x in inp.lengths])
     attn_ms = mean_span(evs, 1, 2)
     return {
@@ -278,6 +287,8 @@ def bench_training_shape(torch, hs, W, steps, warmup):
         "attn_kernel_ms": round(attn_ms, 4),
         "epilogue_ms": round(mean_span(evs, 2, 3), 4),
         "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+        "graph_ms_per_step": round(graph_ms, 4),
+        "graph_tflops": round(flop / (graph_ms * 1e-3) / 1e12, 2),
         "attn_kernel_tflops": round(flop / (attn_ms * 1e-3) / 1e12, 2),
         "algorithmic_gflop": round(flop / 1e9, 3),
     }
