@@ -13,7 +13,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests fail loudly (not skip) when the library is missing on a GPU machine;
+    # GPU tests fail loudly (not skip) when the library is missing on a machine
+    # with a GPU;
     # on a machine without a GPU they are skipped.
     try:
         import torch
