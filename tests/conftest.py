@@ -14,8 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests fail loudly (not skip) when the library is missing on a machine
-    # with a GPU;
-    # on a machine without a GPU they are skipped.
+    # with a GPU; on a machine without a GPU they are skipped.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
