@@ -116,6 +116,23 @@ def test_long_sequences_sampled_rows():
     assert np.isfinite(y).all()
 
 
+def test_more_than_4096_items_sampled_rows():
+    """64 users x 8 heads: 4,608 work items, more than the scheduler keeps in
+    registers between its histogram and scatter passes (the rest are rebuilt)."""
+    rng = np.random.default_rng(133)
+    lengths = [int(x) for x in rng.integers(1025, 1153, size=64)]   # 9 query tiles each
+    inp = W.jagged("many_items", 133, lengths, 8, 64, "bf16", 128, 128)
+    assert sum(8 * ((L + 127) // 128) for L in lengths) > 4096
+    y = to_np(run_full(inp))
+    rows = np.unique(np.concatenate([[0, inp.total - 1], rng.integers(0, inp.total, size=40)]))
+    y_ref = oracle.hstu_full_rows(rows, inp.q, inp.k, inp.v, inp.u, inp.ts, inp.seq_offsets, inp.tables.pos,
+                                  inp.tables.time)
+    err = oracle.max_rel_row_error(y[rows], y_ref)
+    print(f"4,608 items sampled rows max row rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    assert np.isfinite(y).all()
+
+
 # ---------------------------------------------------------------- invariants
 
 def test_jagged_batch_equals_per_sequence_bitwise():
@@ -223,6 +240,20 @@ def test_cached_edge_cases(dtype, d):
     y_ref, _ = oracle.hstu_cached(h.q[new], h.u[new], h.ts[new], h.k, h.v, h.ts, h.seq_offsets, ci.cache_lens,
                                   ci.new_offsets(), h.tables.pos, h.tables.time)
     check(y, y_ref, dtype, f"cached edges {dtype}")
+
+
+def test_cached_more_than_64_users():
+    """70 users: the epilogue finds a row's user by a loop over 64-entry blocks
+    of the offsets (one wave-wide load covers up to 64 users)."""
+    rng = np.random.default_rng(134)
+    cache_lens = [int(x) for x in rng.integers(0, 300, size=70)]
+    new_lens = [int(x) for x in rng.integers(0, 40, size=70)]
+    ci = W.cached("cmany", 134, cache_lens, new_lens, H=2, d=64, dtype="bf16", n_pos=128, n_time=64)
+    y, new = _run_cached(ci)
+    h = ci.hist
+    y_ref, _ = oracle.hstu_cached(h.q[new], h.u[new], h.ts[new], h.k, h.v, h.ts, h.seq_offsets, ci.cache_lens,
+                                  ci.new_offsets(), h.tables.pos, h.tables.time)
+    check(y, y_ref, "bf16", "cached 70 users")
 
 
 def test_cached_equals_gpu_full_path():
