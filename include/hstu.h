@@ -39,6 +39,9 @@
  *     synchronisation and allocates nothing: the caller owns all buffers,
  *     including the workspace. Calls with different workspaces may run
  *     concurrently; calls sharing a workspace must be ordered on one stream.
+ *     No call records a memset, so a caller may capture a sequence of calls
+ *     (for example hstu_kv_append then hstu_attn_fwd_cached) into a HIP graph
+ *     and replay it; the buffers named at capture time are the ones used.
  *   - Errors: argument checks run on the host before anything is launched and
  *     return a status; nothing is launched then. HSTU_ERR_LAUNCH reports a
  *     failed kernel launch. Device-side content (offsets, lengths, page
