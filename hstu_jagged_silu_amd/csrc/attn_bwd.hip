@@ -692,7 +692,17 @@ __global__ __launch_bounds__(64 * RAB_GROUPS) void rab_reduce_kernel(RabReduceAr
   float sum = 0.0f;
   if (c < n && (is_pos || c < 64)) {
     const int slot = is_pos ? c : BWD_MAX_NPOS + c;
-    for (int64_t i = lo + grp; i < hi; i += RAB_GROUPS) sum += a.part[i * RAB_SLOTS + slot];
+    // 16 items' loads in flight before their adds; the adds keep item order
+    constexpr int U = 16;
+    int64_t i = lo + grp;
+    for (; i + (U - 1) * RAB_GROUPS < hi; i += U * RAB_GROUPS) {
+      float x[U];
+      #pragma unroll
+      for (int j = 0; j < U; ++j) x[j] = a.part[(i + j * RAB_GROUPS) * RAB_SLOTS + slot];
+      #pragma unroll
+      for (int j = 0; j < U; ++j) sum += x[j];
+    }
+    for (; i < hi; i += RAB_GROUPS) sum += a.part[i * RAB_SLOTS + slot];
   }
   acc[grp][cl] = sum;
   __syncthreads();
