@@ -155,7 +155,23 @@ __global__ __launch_bounds__(64 * RED_GROUPS) void ln_affine_reduce_kernel(LnBwd
   const int c = blockIdx.x * 64 + cl;
   float sw = 0.0f, sb = 0.0f;
   if (c < a.HD && a.part) {
-    for (int w = grp; w < a.nwaves; w += RED_GROUPS) {
+    // 16 partials' loads in flight before their adds; the adds keep order
+    constexpr int U = 16;
+    int w = grp;
+    for (; w + (U - 1) * RED_GROUPS < a.nwaves; w += U * RED_GROUPS) {
+      float xw[U], xb[U];
+      #pragma unroll
+      for (int j = 0; j < U; ++j) {
+        xw[j] = a.part[(int64_t)(w + j * RED_GROUPS) * a.HD + c];
+        xb[j] = a.part[((int64_t)a.nwaves + w + j * RED_GROUPS) * a.HD + c];
+      }
+      #pragma unroll
+      for (int j = 0; j < U; ++j) {
+        sw += xw[j];
+        sb += xb[j];
+      }
+    }
+    for (; w < a.nwaves; w += RED_GROUPS) {
       sw += a.part[(int64_t)w * a.HD + c];
       sb += a.part[((int64_t)a.nwaves + w) * a.HD + c];
     }
