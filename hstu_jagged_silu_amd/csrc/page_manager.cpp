@@ -11,7 +11,9 @@
 // writes and the cached attention reads; here only page ids move.
 //
 // State: a user (64-bit id) owns a slot = one row of the page table, its
-// cached length and the ordered list of its pages. Free pages form a stack.
+// cached length and the ordered list of its pages (a prefix of the row: the
+// committed pages, then those of a reservation not yet committed). Free pages
+// form a stack.
 // Every lookup, and every user of a reserve in batch order, stamps the slot
 // with the next value of a logical clock; eviction takes the smallest stamp
 // among users not pinned by the current request.
@@ -101,27 +103,41 @@ hstu_status_t hstu_pm_reserve(hstu_page_manager_t* m, int32_t batch, const int64
   std::vector<int32_t> slot(batch, -1);
   std::vector<uint8_t> pinned(m->max_users, 0);  // the batch's resident users are never evicted
   std::unordered_map<int64_t, int32_t> seen;
-  int64_t need_new_slots = 0, need_pages = 0, pinned_slots = 0, pinned_pages = 0;
+  int64_t need_new_slots = 0, pinned_slots = 0, want_pages = 0, need_pages = 0;
   for (int32_t i = 0; i < batch; ++i) {
     if (n_new[i] < 0) return HSTU_ERR_INVALID_ARG;
     if (!seen.emplace(user_ids[i], i).second) return HSTU_ERR_INVALID_ARG;  // one entry per user
     auto f = m->slot_of.find(user_ids[i]);
     const int64_t have = f == m->slot_of.end() ? 0 : m->len[f->second];
-    if (pages_for(m, have + n_new[i]) > m->max_pages) return HSTU_ERR_UNSUPPORTED;  // history too long
+    const int32_t want = pages_for(m, have + n_new[i]);
+    if (want > m->max_pages) return HSTU_ERR_UNSUPPORTED;  // history too long
+    want_pages += want;
     if (f == m->slot_of.end()) {
       ++need_new_slots;
+      need_pages += want;
     } else {
       slot[i] = f->second;
       pinned[f->second] = 1;
       ++pinned_slots;
+      // pages of an earlier reservation that was never committed are reused
       const int32_t* row = m->table.data() + (size_t)f->second * m->max_pages;
-      for (int32_t pg = 0; pg < m->max_pages; ++pg) pinned_pages += row[pg] >= 0;
+      for (int32_t pg = 0; pg < want; ++pg) need_pages += row[pg] < 0;
     }
-    need_pages += pages_for(m, have + n_new[i]) - pages_for(m, have);
   }
-  // what eviction of every other user could free
-  if (need_new_slots > m->max_users - pinned_slots || need_pages > m->num_pages - pinned_pages)
-    return HSTU_ERR_WORKSPACE;
+  // after the request the batch's users hold exactly want_pages pages; every
+  // other user can be evicted
+  if (need_new_slots > m->max_users - pinned_slots || want_pages > m->num_pages) return HSTU_ERR_WORKSPACE;
+  // from here on the request succeeds. Pages a resident user holds beyond its
+  // new page count (a larger reservation that was never committed) go back to
+  // the pool first.
+  for (int32_t i = 0; i < batch; ++i) {
+    if (slot[i] < 0) continue;
+    int32_t* row = m->table.data() + (size_t)slot[i] * m->max_pages;
+    for (int32_t pg = pages_for(m, (int64_t)m->len[slot[i]] + n_new[i]); pg < m->max_pages; ++pg) {
+      if (row[pg] >= 0) m->free_pages.push_back(row[pg]);
+      row[pg] = -1;
+    }
+  }
   // evict unpinned users, least recently used first, until the free slots
   // and pages cover the request
   while ((int64_t)m->free_slots.size() < need_new_slots || (int64_t)m->free_pages.size() < need_pages) {
@@ -143,8 +159,9 @@ hstu_status_t hstu_pm_reserve(hstu_page_manager_t* m, int32_t batch, const int64
     }
     m->stamp[s] = ++m->clock;
     int32_t* row = m->table.data() + (size_t)s * m->max_pages;
-    const int32_t have = pages_for(m, m->len[s]), want = pages_for(m, (int64_t)m->len[s] + n_new[i]);
-    for (int32_t pg = have; pg < want; ++pg) {
+    const int32_t want = pages_for(m, (int64_t)m->len[s] + n_new[i]);
+    for (int32_t pg = 0; pg < want; ++pg) {
+      if (row[pg] >= 0) continue;  // committed, or reserved earlier and not committed
       row[pg] = m->free_pages.back();
       m->free_pages.pop_back();
     }

@@ -341,6 +341,11 @@ hstu_status_t hstu_mfalcon_fwd_cached(const hstu_params_t* params, int32_t batch
  *      comes back with cached length 0: the caller sends its whole history.
  *   2. per layer: hstu_kv_append, then hstu_attn_fwd_cached.
  *   3. hstu_pm_commit(batch ids, new token counts) advances the lengths.
+ * A reserve replaces the user's earlier reservation if that was never
+ * committed (or committed for fewer tokens): the row then holds exactly
+ * ceil((cached length + new tokens) / 64) pages, reusing the pages reserved
+ * before and returning the rest to the pool. Reserved pages are never lost:
+ * they stay with the user until its next reserve or its eviction.
  * Every lookup, and every user of a reserve in batch order, counts as a use;
  * eviction takes the least recently used user outside the request. Users of
  * the batch are never evicted by their own reserve. A reserve that

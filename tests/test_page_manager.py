@@ -1,7 +1,8 @@
 """Host logic of the paged KV-cache manager (hstu_pm_*, no GPU): allocation,
 growth across page boundaries, LRU eviction, pinning of the request's own
-users, failure atomicity, and a randomized comparison with a small Python
-model of the documented rules."""
+users, failure atomicity, reservations that are replaced or only partly
+committed, and a randomized comparison with a small Python model of the
+documented rules."""
 import numpy as np
 import pytest
 
@@ -86,12 +87,15 @@ class Model:
         if any(pages(have[u] + n) > self.M for u, n in zip(ids, n_new)):
             return "UNSUPPORTED", None
         need_slots = sum(u not in self.len for u in ids)
-        need_pages = sum(pages(have[u] + n) - pages(have[u]) for u, n in zip(ids, n_new))
+        # after the call the batch's users hold exactly pages(len + n) pages
+        # each (a reservation never committed is replaced, not added to)
+        want = sum(pages(have[u] + n) for u, n in zip(ids, n_new))
         pinned = [u for u in ids if u in self.len]
-        if need_slots > self.U - len(pinned) or need_pages > self.P - sum(self.npages[u] for u in pinned):
+        if need_slots > self.U - len(pinned) or want > self.P:
             return "WORKSPACE", None
         ev = 0
-        while (self.U - len(self.len) < need_slots) or (self.P - self.used_pages() < need_pages):
+        others = lambda: sum(p for u, p in self.npages.items() if u not in ids)
+        while (self.U - len(self.len) < need_slots) or (others() + want > self.P):
             victim = min((u for u in self.len if u not in pinned), key=lambda u: self.last[u])
             del self.len[victim], self.npages[victim], self.last[victim]
             ev += 1
@@ -132,7 +136,54 @@ def test_randomized_against_model():
             k = pages(res[0][i] + n)
             assert (table[i, :k] >= 0).all() and (table[i, k:] == -1).all()
         assert len(set(table[table >= 0].tolist())) == int((table >= 0).sum())
-        pm.commit(ids, n_new)
-        ref.commit(ids, n_new)
+        # commit all, part (fewer tokens than reserved) or nothing (an
+        # abandoned reservation, replaced by the user's next reserve)
+        r = rng.random()
+        if r < 0.6:
+            done = n_new
+        elif r < 0.8:
+            done = [int(rng.integers(0, n + 1)) for n in n_new]
+        else:
+            done = None
+        if done is not None:
+            pm.commit(ids, done)
+            ref.commit(ids, done)
         st = pm.stats()
         assert st["users"] == len(ref.len) and st["free_pages"] == P - ref.used_pages()
+    for u in list(ref.len):
+        pm.evict(u)
+    assert pm.stats()["free_pages"] == P and pm.stats()["users"] == 0
+
+
+def test_repeated_reserve_reuses_pages():
+    # two reserves without a commit between them: the second reuses the
+    # first's pages, and eviction returns every page to the pool
+    pm = hs.PageManager(num_pages=6, max_pages_per_seq=4, max_users=2)
+    _, t1, _ = pm.reserve([1], [130])                   # 3 pages
+    assert pm.stats()["free_pages"] == 3
+    _, t2, _ = pm.reserve([1], [130])                   # the same 3 pages again
+    assert list(t2[0]) == list(t1[0]) and pm.stats()["free_pages"] == 3
+    _, t3, _ = pm.reserve([1], [10])                    # a smaller request gives 2 back
+    assert list(t3[0, :1]) == list(t1[0, :1]) and (t3[0, 1:] == -1).all()
+    assert pm.stats()["free_pages"] == 5
+    pm.commit([1], [10])
+    assert pm.lookup(1) == 10
+    _, t4, _ = pm.reserve([1], [200])                   # 210 tokens: 4 pages, the first kept
+    assert t4[0, 0] == t1[0, 0] and (t4[0] >= 0).all() and len(set(t4[0].tolist())) == 4
+    pm.commit([1], [100])                               # part of the reservation
+    assert pm.stats()["free_pages"] == 2                # the 4th page stays reserved
+    pm.evict(1)
+    assert pm.stats() == {"free_pages": 6, "users": 0, "evictions": 1}
+
+
+def test_reserve_twice_then_full_pool():
+    # a reservation that is replaced must not shrink the pool: after it the
+    # whole pool still fits one request
+    pm = hs.PageManager(num_pages=4, max_pages_per_seq=4, max_users=2)
+    pm.reserve([1], [256])
+    pm.reserve([1], [256])
+    pm.commit([1], [256])
+    assert pm.stats()["free_pages"] == 0
+    pm.evict(1)
+    lens, table, ev = pm.reserve([2], [256])
+    assert ev == 0 and (table[0] >= 0).all() and pm.stats()["free_pages"] == 0
