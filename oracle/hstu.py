@@ -60,7 +60,8 @@ __all__ = [
     "time_bucket", "pos_bucket", "silu", "layer_norm_gate",
     "hstu_full", "hstu_full_rows", "hstu_cached", "hstu_mfalcon",
     "kv_append_pages", "hstu_layer", "max_rel_row_error", "pair_count",
-    "silu_grad", "layer_norm_gate_bwd", "hstu_full_bwd", "max_rel_err_vs_magnitude", "dense",
+    "silu_grad", "layer_norm_gate_bwd", "hstu_full_bwd", "max_rel_err_vs_magnitude", "max_err_vs_scale",
+    "dense",
 ]
 
 
@@ -437,7 +438,7 @@ def layer_norm_gate_bwd(z, u, dy, gamma=None, beta=None, eps=1e-5):
 
 
 def hstu_full_bwd(q, k, v, u, ts, seq_offsets, dy, pos_tab=None, time_tab=None, alpha=1.0, norm_n=0,
-                  gamma=None, beta=None, eps=1e-5, magnitudes=False):
+                  gamma=None, beta=None, eps=1e-5, magnitudes=False, pair_mask=None):
     """Gradients of the full causal path (hstu_full) for an upstream gradient dy [T, H*d].
 
     Per sequence and head, with s = alpha q k^T + bias, a = SiLU(s) / N on
@@ -456,7 +457,24 @@ def hstu_full_bwd(q, k, v, u, ts, seq_offsets, dy, pos_tab=None, time_tab=None, 
     sums taken over absolute values (|do| |v|^T for da, |da| |SiLU'| / N for
     ds, and so on): the scale against which rounding errors of the summed
     terms are measured (a gradient that is small only by cancellation has a
-    large magnitude).
+    large magnitude). It also holds, under "rss_<name>" for dq, dk, dv, dpos
+    and dtime, the root-sum-square of the terms: every gradient entry written
+    out as one sum of products of leaf factors (dq_ic = alpha / N * sum over
+    keys j and features e of SiLU'(s_ij) do_ie v_je k_jc; dv_jc = sum over i
+    of a_ij do_ic; a table entry = sum over its pairs and features of
+    SiLU'(s_ij) do_ie v_je / N; and each do_ie itself written out as the
+    terms of the norm's backward, r (g_e - mean g - n_e mean(g n)) with
+    g = dY u gamma), with each term squared, the squares added, and the
+    root taken. Independent relative rounding errors of size eps per
+    term give an error whose spread is about eps times this scale, whatever
+    the signs, so it is the natural unit for a rounding error; a term that
+    is missing altogether costs about its own size, which on random data is
+    the scale itself.
+
+    pair_mask, when given, is called as pair_mask(b, allowed) for sequence b
+    and returns the pairs the gradient sums keep (a subset of ``allowed``);
+    the recomputed forward is not affected. Tests use it to show what a
+    backward that skips pairs (one key tile, say) would return.
     """
     H, d = _heads(q)
     T = q.shape[0]
@@ -470,11 +488,30 @@ def hstu_full_bwd(q, k, v, u, ts, seq_offsets, dy, pos_tab=None, time_tab=None, 
     dpos = None if pos_tab is None else np.zeros(np.shape(pos_tab))
     dtime = None if time_tab is None else np.zeros(np.shape(time_tab))
     mag = {}
+    do_r2 = None
     if magnitudes:
+        # dO written out as the terms of the norm's backward, r (g_c - mean_e
+        # g_e - n_c mean_e g_e n_e) with g = dY u gamma: the sum of their
+        # squares stands for dO^2 in the root-sum-square of everything
+        # downstream (dO's own size can be small by cancellation while its
+        # terms, and any error they carry, are not)
+        z = np.asarray(o, dtype=np.float64)
+        D = z.shape[-1]
+        mu = z.mean(axis=-1, keepdims=True)
+        rr = 1.0 / np.sqrt(((z - mu) ** 2).mean(axis=-1, keepdims=True) + eps)
+        nn = (z - mu) * rr
+        gg = np.asarray(dy, dtype=np.float64) * np.asarray(u, dtype=np.float64)
+        if gamma is not None:
+            gg = gg * np.asarray(gamma, dtype=np.float64)
+        do_r2 = (rr ** 2 * (gg ** 2 + (gg ** 2).sum(axis=-1, keepdims=True) / D ** 2
+                            + nn ** 2 * ((gg * nn) ** 2).sum(axis=-1, keepdims=True) / D ** 2)).reshape(T, H, d)
         mag = {"mag_dq": np.zeros((T, H, d)), "mag_dk": np.zeros((T, H, d)), "mag_dv": np.zeros((T, H, d)),
                "mag_du": np.abs(du),
                "mag_dpos": None if dpos is None else np.zeros_like(dpos),
                "mag_dtime": None if dtime is None else np.zeros_like(dtime)}
+        mag.update({"rss_dq": np.zeros((T, H, d)), "rss_dk": np.zeros((T, H, d)), "rss_dv": np.zeros((T, H, d)),
+                    "rss_dpos": None if dpos is None else np.zeros_like(dpos),
+                    "rss_dtime": None if dtime is None else np.zeros_like(dtime)})
         if dgamma is not None or dbeta is not None:
             z = np.asarray(o, dtype=np.float64)
             mu = z.mean(axis=-1, keepdims=True)
@@ -491,6 +528,7 @@ def hstu_full_bwd(q, k, v, u, ts, seq_offsets, dy, pos_tab=None, time_tab=None, 
         allowed = pos[None, :] <= pos[:, None]
         n_norm = norm_n if norm_n > 0 else L
         rel = np.where(allowed, pos[:, None] - pos[None, :], 0)
+        kept = allowed if pair_mask is None else (np.asarray(pair_mask(b, allowed.copy()), dtype=bool) & allowed)
         t = np.asarray(ts[s0:s1], dtype=np.int64)
         dt = t[:, None] - t[None, :]
         for h in range(H):
@@ -502,24 +540,38 @@ def hstu_full_bwd(q, k, v, u, ts, seq_offsets, dy, pos_tab=None, time_tab=None, 
             doh = do[s0:s1, h]
             dv[s0:s1, h] = a.T @ doh
             da = doh @ vh.T
-            ds = np.where(allowed, da * silu_grad(s), 0.0) / float(n_norm)
+            ds = np.where(kept, da * silu_grad(s), 0.0) / float(n_norm)
+            if pair_mask is not None:
+                dv[s0:s1, h] = np.where(kept, a, 0.0).T @ doh
             dq[s0:s1, h] = alpha * (ds @ kh)
             dk[s0:s1, h] = alpha * (ds.T @ qh)
             if dpos is not None:
                 row = dpos if dpos.ndim == 1 else dpos[h]
-                np.add.at(row, pos_bucket(rel[allowed], row.shape[0]), ds[allowed])
+                np.add.at(row, pos_bucket(rel[kept], row.shape[0]), ds[kept])
             if dtime is not None:
                 row = dtime if dtime.ndim == 1 else dtime[h]
-                np.add.at(row, time_bucket(dt[allowed], row.shape[0]), ds[allowed])
+                np.add.at(row, time_bucket(dt[kept], row.shape[0]), ds[kept])
             if magnitudes:
                 ds_m = np.where(allowed, (np.abs(doh) @ np.abs(vh).T) * np.abs(silu_grad(s)), 0.0) / float(n_norm)
                 mag["mag_dq"][s0:s1, h] = abs(alpha) * (ds_m @ np.abs(kh))
                 mag["mag_dk"][s0:s1, h] = abs(alpha) * (ds_m.T @ np.abs(qh))
                 mag["mag_dv"][s0:s1, h] = np.abs(a).T @ np.abs(doh)
-                for key, rel_or_dt, fn in (("mag_dpos", rel, pos_bucket), ("mag_dtime", dt, time_bucket)):
+                # squared root-sum-square of the terms of each ds_ij, then of
+                # each gradient entry (sums of squares of the same terms)
+                dor2 = do_r2[s0:s1, h]
+                ds_r2 = np.where(allowed, (dor2 @ (vh ** 2).T) * silu_grad(s) ** 2, 0.0) / float(n_norm) ** 2
+                mag["rss_dq"][s0:s1, h] = abs(alpha) * np.sqrt(ds_r2 @ kh ** 2)
+                mag["rss_dk"][s0:s1, h] = abs(alpha) * np.sqrt(ds_r2.T @ qh ** 2)
+                mag["rss_dv"][s0:s1, h] = np.sqrt((a ** 2).T @ dor2)
+                for key, rel_or_dt, fn, w in (("mag_dpos", rel, pos_bucket, ds_m), ("mag_dtime", dt, time_bucket, ds_m),
+                                              ("rss_dpos", rel, pos_bucket, ds_r2),
+                                              ("rss_dtime", dt, time_bucket, ds_r2)):
                     if mag[key] is not None:
                         row = mag[key] if mag[key].ndim == 1 else mag[key][h]
-                        np.add.at(row, fn(rel_or_dt[allowed], row.shape[0]), ds_m[allowed])
+                        np.add.at(row, fn(rel_or_dt[allowed], row.shape[0]), w[allowed])
+    for key in ("rss_dpos", "rss_dtime"):  # sums of squares so far
+        if mag.get(key) is not None:
+            mag[key] = np.sqrt(mag[key])
     out = {"dq": dq, "dk": dk, "dv": dv, "du": du, "dpos": dpos, "dtime": dtime,
            "dgamma": dgamma, "dbeta": dbeta}
     out.update(mag)
@@ -569,6 +621,25 @@ def max_rel_err_vs_magnitude(g, g_ref, mag):
     if np.any(zero & (num > 0)):
         return float("inf")
     return float(np.where(zero, 0.0, num / np.where(zero, 1.0, den)).max()) if n else 0.0
+
+
+def max_err_vs_scale(g, g_ref, scale):
+    """max over entries of |g - g*| / scale, entry by entry.
+
+    scale has g*'s shape (the root-sum-square of each entry's terms, say).
+    Entries whose scale is zero are sums of no terms and must be exactly zero
+    in g as well (else inf). Empty inputs give 0.
+    """
+    g = np.asarray(g, dtype=np.float64).reshape(-1)
+    g_ref = np.asarray(g_ref, dtype=np.float64).reshape(-1)
+    scale = np.asarray(scale, dtype=np.float64).reshape(-1)
+    if g_ref.size == 0:
+        return 0.0
+    err = np.abs(g - g_ref)
+    zero = scale == 0
+    if np.any(zero & (err > 0)):
+        return float("inf")
+    return float(np.where(zero, 0.0, err / np.where(zero, 1.0, scale)).max())
 
 
 def pair_count(kind, lengths, extra=None):

@@ -5,7 +5,7 @@ import torch
 
 import hstu_jagged_silu_amd as hs
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
+from tolerances import GRAD_RSS_BF16, TOL  # noqa: F401
 
 
 def tdtype(name):

@@ -1,15 +1,18 @@
 """GPU parity of the backward (hstu_attn_bwd) against the fp64 oracle's
 hstu_full_bwd, through the C ABI.
 
-Error metric: per output, max over rows of ||g - g*||_inf / ||m*||_inf, where
-m* is the oracle's same sum over absolute values of the terms (its
-"magnitude"; bias tables and affine terms are one row each). A gradient
-entry is a sum of products whose factors reach the MFMAs rounded to bf16
-(dO, P, dS; relative error at most 2^-8 each) and is returned rounded to
-bf16, so its error is bounded by a few times 2^-8 of that magnitude; the
-bar is 2e-2 (about 5 x 2^-8), the forward's bf16 bar. Measuring against the
-value itself instead would fail rows whose gradient is small only through
-cancellation (the first token of a user, for one)."""
+Error metrics:
+* dQ, dK, dV and the bias-table gradients, entry by entry: |g - g*| over the
+  root-sum-square of the entry's terms (the oracle's "rss_<name>"), bar
+  GRAD_RSS_BF16 = 8 x 2^-8. Each term reaches the sum through at most four
+  bf16 roundings (dO, P or dS, the returned value), so the error spreads as
+  about 1.15 x 2^-8 of that scale whatever the signs; the bar is about seven
+  such spreads. A key tile that the kernel skips scores far above it (a CPU
+  pin shows a dropped 64-key tile failing it by more than ten times).
+* dU and the norm's affine gradients, per row: ||g - g*||_inf over the
+  oracle's same sum over absolute values (a single product for dU; sums over
+  tokens for the affine terms), bar 2e-2, the forward's bf16 bar.
+"""
 import numpy as np
 import pytest
 import torch
@@ -18,7 +21,7 @@ import hstu_jagged_silu_amd as hs
 import oracle
 import workloads as W
 
-from devutil import TOL, dev, to_np
+from devutil import GRAD_RSS_BF16, TOL, dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -43,22 +46,24 @@ def run_bwd(inp, dy, per_head_tables=False, affine=None, alpha=1.0, norm_n=0, ta
     return g, ref
 
 
-def check(g, ref, tol=TOL["bf16"], label=""):
-    errs = {}
+def check(g, ref, label=""):
+    errs, bars = {}, {}
     for name, rname in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("du", "du"), ("d_pos_tab", "dpos"),
                         ("d_time_tab", "dtime"), ("d_ln_w", "dgamma"), ("d_ln_b", "dbeta")):
         if ref[rname] is None:
             assert g[name] is None, name
             continue
         r = np.asarray(ref[rname])
-        m = np.asarray(ref["mag_" + rname])
-        x = to_np(g[name])
-        if rname in ("dq", "dk", "dv"):
-            x, r, m = (t.reshape(r.shape[0], -1) for t in (x, r, m))
-        errs[name] = oracle.max_rel_err_vs_magnitude(x, r, m)
-    print(label, " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+        x = to_np(g[name]).reshape(r.shape)
+        if "rss_" + rname in ref:
+            errs[name] = oracle.max_err_vs_scale(x, r, ref["rss_" + rname])
+            bars[name] = GRAD_RSS_BF16
+        else:
+            errs[name] = oracle.max_rel_err_vs_magnitude(x, r, np.asarray(ref["mag_" + rname]))
+            bars[name] = TOL["bf16"]
+    print(label, " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
     for k, v in errs.items():
-        assert v <= tol, (k, v)
+        assert v <= bars[k], (k, v, bars[k])
 
 
 @pytest.mark.parametrize("d", [128, 64, 32])

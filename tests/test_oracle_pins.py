@@ -428,13 +428,104 @@ def test_max_rel_row_error():
     assert oracle.max_rel_row_error(ref + [[0, 0], [0, 1e-3]], ref) == float("inf")
 
 
+def test_max_err_vs_scale_hand_computed():
+    g_ref = np.array([1.5, 2.0, 0.0, -4.0])
+    g = np.array([1.0, 2.0, 0.0, -3.0])
+    scale = np.array([2.0, 1.0, 0.0, 8.0])
+    # entries: 0.5 / 2, 0 / 1, exact zero with zero scale, 1 / 8
+    assert oracle.max_err_vs_scale(g, g_ref, scale) == 0.25
+    assert oracle.max_err_vs_scale(g.reshape(2, 2), g_ref.reshape(2, 2), scale.reshape(2, 2)) == 0.25
+    bad = g.copy()
+    bad[2] = 1e-30                                      # nonzero where no term exists
+    assert oracle.max_err_vs_scale(bad, g_ref, scale) == float("inf")
+    assert oracle.max_err_vs_scale(np.zeros(0), np.zeros(0), np.zeros(0)) == 0.0
+
+
+def test_max_rel_err_vs_magnitude_hand_computed():
+    g_ref = np.array([[1.0, 1.0], [3.0, 3.0]])
+    g = np.array([[1.0, 2.0], [3.0, 4.0]])
+    mag = np.array([[2.0, 4.0], [1.0, 8.0]])
+    # row 0: max |diff| 1 over max magnitude 4; row 1: 1 over 8
+    assert oracle.max_rel_err_vs_magnitude(g, g_ref, mag) == 0.25
+    # a 1-D input is one row: max |diff| 1 over max magnitude 8
+    assert oracle.max_rel_err_vs_magnitude(g.reshape(-1), g_ref.reshape(-1), mag.reshape(-1)) == 0.125
+    assert oracle.max_rel_err_vs_magnitude(g, g_ref, np.array([[0.0, 0.0], [1.0, 8.0]])) == float("inf")
+
+
+def _count_pairs_from_oracle_masks(kind, lengths, extra):
+    """Pairs the oracle's own masks allow, read off its pre-norm output.
+
+    With q = k = 0, v = 1, no time table and a constant position table c,
+    every allowed pair contributes SiLU(c) / N to each feature of its row's
+    output, so row i's output times N / SiLU(c) is its number of keys.
+    """
+    c = 1.5
+    sc = c / (1 + np.exp(-c))
+    H, d = 1, 2
+    ptab = np.full(4, c)
+    if kind == "full":
+        T = sum(lengths)
+        off = np.concatenate([[0], np.cumsum(lengths)])
+        z = np.zeros((T, H, d))
+        _, o = oracle.hstu_full(z, z, np.ones((T, H, d)), np.ones((T, H * d)), np.arange(T), off, ptab, None,
+                                norm_n=1)
+    elif kind == "cached":
+        new, cache = list(lengths), list(extra)
+        M, K = sum(new), sum(a + b for a, b in zip(new, cache))
+        noff = np.concatenate([[0], np.cumsum(new)])
+        hoff = np.concatenate([[0], np.cumsum([a + b for a, b in zip(new, cache)])])
+        _, o = oracle.hstu_cached(np.zeros((M, H, d)), np.ones((M, H * d)), np.arange(M), np.zeros((K, H, d)),
+                                  np.ones((K, H, d)), np.arange(K), hoff, cache, noff, ptab, None, norm_n=1)
+    else:
+        hist, cand = list(lengths), list(extra)
+        L = [a + b for a, b in zip(hist, cand)]
+        T = sum(L)
+        off = np.concatenate([[0], np.cumsum(L)])
+        z = np.zeros((T, H, d))
+        _, o = oracle.hstu_mfalcon(z, z, np.ones((T, H, d)), np.ones((T, H * d)), np.arange(T), off, cand, ptab,
+                                   None, norm_n=1)
+    per_row = np.asarray(o)[:, 0] / sc
+    assert np.allclose(per_row, np.round(per_row))
+    return int(round(per_row.sum()))
+
+
 def test_pair_counts():
     assert oracle.pair_count("full", [8192] * 8) == 268_468_224
     assert oracle.pair_count("cached", [128] * 8, [8192] * 8) == 8 * (128 * 8192 + 128 * 129 // 2)
     assert oracle.pair_count("mfalcon", [4096] * 4, [1024] * 4) == 4 * (4096 * 4097 // 2 + 1024 * 4097)
-    # brute force over tiny masks
-    L = 7
-    assert oracle.pair_count("full", [L]) == sum(1 for i in range(L) for j in range(L) if j <= i)
+
+
+@pytest.mark.parametrize("lengths", [[7], [0, 1, 5, 3], [2, 0]])
+def test_pair_count_full_enumerated(lengths):
+    # causal: every key at or before the query
+    brute = sum(1 for L in lengths for i in range(L) for j in range(L) if j <= i)
+    assert oracle.pair_count("full", lengths) == brute
+    assert _count_pairs_from_oracle_masks("full", lengths, None) == brute
+
+
+@pytest.mark.parametrize("new,cache", [([3], [5]), ([1, 4, 0], [0, 2, 6]), ([2, 2], [64, 1])])
+def test_pair_count_cached_enumerated(new, cache):
+    # new token m of a user with C cached tokens sits at position C + m and
+    # sees keys 0 .. C + m of the C + M key sequence
+    brute = sum(1 for M, C in zip(new, cache) for m in range(M) for j in range(C + M) if j <= C + m)
+    assert oracle.pair_count("cached", new, cache) == brute
+    assert _count_pairs_from_oracle_masks("cached", new, cache) == brute
+
+
+@pytest.mark.parametrize("hist,cand", [([4], [3]), ([0, 3, 5], [2, 0, 1]), ([6, 1], [1, 4])])
+def test_pair_count_mfalcon_enumerated(hist, cand):
+    # history rows causal over the history; a candidate sees the whole
+    # history and itself, never another candidate
+    brute = 0
+    for n, m in zip(hist, cand):
+        for i in range(n + m):
+            for j in range(n + m):
+                if i < n:
+                    brute += j <= i
+                else:
+                    brute += j < n or j == i
+    assert oracle.pair_count("mfalcon", hist, cand) == brute
+    assert _count_pairs_from_oracle_masks("mfalcon", hist, cand) == brute
 
 
 def test_dense_matches_loops_and_split_order():
