@@ -32,7 +32,8 @@ PAGE_SIZE = 64
 
 EXPORTED_SYMBOLS = (
     "hstu_status_string", "hstu_version", "hstu_workspace_size", "hstu_attn_fwd",
-    "hstu_kv_append", "hstu_attn_fwd_cached", "hstu_mfalcon_fwd", "hstu_mfalcon_fwd_cached", "hstu_attn_bwd",
+    "hstu_kv_append", "hstu_attn_fwd_cached", "hstu_attn_fwd_cached_noalloc", "hstu_mfalcon_fwd",
+    "hstu_mfalcon_fwd_cached", "hstu_attn_bwd",
     "hstu_layer_workspace_size", "hstu_matmul_bf16",
     "hstu_layer_fwd", "hstu_pm_create", "hstu_pm_destroy", "hstu_pm_reserve", "hstu_pm_commit", "hstu_pm_lookup",
     "hstu_pm_evict", "hstu_pm_stats",
@@ -100,6 +101,8 @@ def _load():
     lib.hstu_kv_append.argtypes = [K, P, i32, vp, vp, i64, vp, vp, vp, vp]
     lib.hstu_attn_fwd_cached.restype = ctypes.c_int
     lib.hstu_attn_fwd_cached.argtypes = [P, i32, vp, vp, i32, i32, i64, vp, vp, vp, K, vp, vp, sz, vp]
+    lib.hstu_attn_fwd_cached_noalloc.restype = ctypes.c_int
+    lib.hstu_attn_fwd_cached_noalloc.argtypes = [P, i32, vp, vp, i32, i32, i64, vp, vp, vp, K, vp, vp]
     lib.hstu_mfalcon_fwd.restype = ctypes.c_int
     lib.hstu_mfalcon_fwd.argtypes = [P, i32, vp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hstu_mfalcon_fwd_cached.restype = ctypes.c_int
@@ -480,6 +483,34 @@ def hstu_attn_fwd_cached(q_new, u_new, ts_new, new_offsets, cache_lens, max_new:
                                      ctypes.byref(c), y.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
            "hstu_attn_fwd_cached")
     return y
+
+
+def hstu_attn_fwd_cached_noalloc(q_new, u_new, ts_new, new_offsets, cache_lens, max_new: int, max_total: int,
+                                 cache: PagedKVCache, params: LayerParams, y, *, timing_events=None):
+    """hstu_attn_fwd_cached for callers that cannot allocate: no workspace
+    argument (the library's per-GPU scratch of HSTU_NOALLOC_SCRATCH_BYTES is
+    used) and the output y is required. Calls on one GPU must be ordered on
+    one stream."""
+    H, d = params.num_heads, params.head_dim
+    _device_tensor(q_new, params.dtype, "q_new")
+    if q_new.dim() != 3 or q_new.shape[1:] != (H, d):
+        raise ValueError(f"q_new must be [T, {H}, {d}]")
+    _device_tensor(u_new, params.dtype, "u_new")
+    _device_tensor(ts_new, torch.int64, "ts_new")
+    _device_tensor(new_offsets, torch.int32, "new_offsets")
+    _device_tensor(cache_lens, torch.int32, "cache_lens")
+    _device_tensor(y, params.dtype, "y")
+    T, B = q_new.shape[0], new_offsets.shape[0] - 1
+    c = cache.c_struct(params)
+    p = params.c_struct(timing_events)
+    _check(_lib.hstu_attn_fwd_cached_noalloc(ctypes.byref(p), B, new_offsets.data_ptr(), cache_lens.data_ptr(),
+                                             max_new, max_total, T, q_new.data_ptr(), u_new.data_ptr(),
+                                             ts_new.data_ptr(), ctypes.byref(c), y.data_ptr(), _stream()),
+           "hstu_attn_fwd_cached_noalloc")
+    return y
+
+
+HSTU_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def hstu_mfalcon_fwd_cached(q, k, v, u, ts, cand_offsets, hist_lens, max_cand: int, max_hist: int,

@@ -1,19 +1,48 @@
 // C ABI of the HSTU attention library: host-side argument checks, workspace
 // layout and the launch sequence of each entry point. No allocation, no host
-// synchronisation; everything is queued on the caller's stream.
+// synchronisation; everything is queued on the caller's stream. The one
+// device buffer the library owns is the scratch array of the no-allocation
+// variant of the cached path.
 #include <cstdlib>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/hstu.h"
 #include "kernels.h"
 
 using namespace hstu;
 
+// Scratch of hstu_attn_fwd_cached_noalloc: one copy on every GPU the library
+// runs on, alive until the process ends. In host code this name is only a
+// handle for hipGetSymbolAddress; the device address comes from there.
+static __device__ __align__(256) unsigned char scratch[HSTU_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+std::atomic<void*> scratch_addr[MAX_DEVICES];  // device address of `scratch`, per device
+
+// Address of the current device's scratch, looked up once per device with
+// that device current; nullptr when the lookup fails.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  void* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  p = scratch_addr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 constexpr int32_t VERSION = 10000;  // 1.0.0
 constexpr int MAX_SPLITS = 16;      // key splits of the cached path
@@ -450,11 +479,17 @@ hstu_status_t hstu_kv_append(const hstu_kv_cache_t* cache, const hstu_params_t* 
   return launch_kv_append(a, stream) == hipSuccess ? HSTU_OK : HSTU_ERR_LAUNCH;
 }
 
-hstu_status_t hstu_attn_fwd_cached(const hstu_params_t* params, int32_t batch, const int32_t* new_offsets,
-                                   const int32_t* cache_lens, int32_t max_new, int32_t max_total,
-                                   int64_t total_new, const void* q_new, const void* u_new,
-                                   const int64_t* ts_new, const hstu_kv_cache_t* cache, void* y_new,
-                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The cached path with its workspace given (ws != nullptr), or with the
+// library's per-device scratch (ws == nullptr; no HIP call before the size
+// check passes).
+hstu_status_t fwd_cached(const hstu_params_t* params, int32_t batch, const int32_t* new_offsets,
+                         const int32_t* cache_lens, int32_t max_new, int32_t max_total, int64_t total_new,
+                         const void* q_new, const void* u_new, const int64_t* ts_new, const hstu_kv_cache_t* cache,
+                         void* y_new, void* ws, size_t ws_bytes, bool use_scratch, hipStream_t stream) {
   hstu_status_t st = check_params(params);
   if (st != HSTU_OK) return st;
   if (!cache) return HSTU_ERR_INVALID_ARG;
@@ -471,6 +506,12 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_params_t* params, int32_t batch, c
   if ((int64_t)cache->max_pages_per_seq * PAGE < max_total) return HSTU_ERR_INVALID_ARG;
   WsLayout w;
   if (!layout(HSTU_FN_CACHED, params, batch, total_new, max_total, w)) return HSTU_ERR_INVALID_ARG;
+  if (use_scratch) {
+    if (w.total > HSTU_NOALLOC_SCRATCH_BYTES) return HSTU_ERR_WORKSPACE;
+    ws = device_scratch();
+    if (!ws) return HSTU_ERR_LAUNCH;
+    ws_bytes = HSTU_NOALLOC_SCRATCH_BYTES;
+  }
   if (!ws || ws_bytes < w.total || !aligned16(ws)) return HSTU_ERR_WORKSPACE;
 
   SchedArgs s = sched_args(MODE_CACHED, params, w, ws, batch, new_offsets, w.chunk_keys);
@@ -505,6 +546,28 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_params_t* params, int32_t batch, c
   chk.max_pages = cache->max_pages_per_seq;
   if (!debug_check(chk, ws, s, stream)) return HSTU_ERR_LAUNCH;
   return run_attention(params, s, a, MODE_CACHED, l, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status_t hstu_attn_fwd_cached(const hstu_params_t* params, int32_t batch, const int32_t* new_offsets,
+                                   const int32_t* cache_lens, int32_t max_new, int32_t max_total,
+                                   int64_t total_new, const void* q_new, const void* u_new,
+                                   const int64_t* ts_new, const hstu_kv_cache_t* cache, void* y_new,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  return fwd_cached(params, batch, new_offsets, cache_lens, max_new, max_total, total_new, q_new, u_new, ts_new,
+                    cache, y_new, ws, ws_bytes, false, stream);
+}
+
+hstu_status_t hstu_attn_fwd_cached_noalloc(const hstu_params_t* params, int32_t batch,
+                                           const int32_t* new_offsets, const int32_t* cache_lens,
+                                           int32_t max_new, int32_t max_total, int64_t total_new,
+                                           const void* q_new, const void* u_new, const int64_t* ts_new,
+                                           const hstu_kv_cache_t* cache, void* y_new, hipStream_t stream) {
+  return fwd_cached(params, batch, new_offsets, cache_lens, max_new, max_total, total_new, q_new, u_new, ts_new,
+                    cache, y_new, nullptr, 0, true, stream);
 }
 
 hstu_status_t hstu_mfalcon_fwd_cached(const hstu_params_t* params, int32_t batch, const int32_t* cand_offsets,

@@ -37,7 +37,8 @@
  *     the page table are device memory too.
  *   - Every call is asynchronous on `stream`, performs no host
  *     synchronisation and allocates nothing: the caller owns all buffers,
- *     including the workspace. Calls with different workspaces may run
+ *     including the workspace (hstu_attn_fwd_cached_noalloc alone uses a
+ *     scratch array the library holds instead). Calls with different workspaces may run
  *     concurrently; calls sharing a workspace must be ordered on one stream.
  *     No call records a memset, so a caller may capture a sequence of calls
  *     (for example hstu_kv_append then hstu_attn_fwd_cached) into a HIP graph
@@ -275,6 +276,29 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_params_t* params, int32_t batch, c
                                    int64_t total_new, const void* q_new, const void* u_new,
                                    const int64_t* ts_new, const hstu_kv_cache_t* cache, void* y_new,
                                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the KV-cache
+ * delta path of hstu_attn_fwd_cached, same arguments and same result, without
+ * the workspace argument. Its scratch is a device array inside the library
+ * of HSTU_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on that GPU
+ * until the process ends; the call itself allocates nothing. A call whose
+ * workspace size (hstu_workspace_size(HSTU_FN_CACHED, ...)) exceeds it
+ * returns HSTU_ERR_WORKSPACE before touching the GPU. The KV-delta serving
+ * shape (8 users x 128 new tokens, 8,192 cached, 4 heads x 128) needs 32.1
+ * MiB. Nothing in the scratch has to start at zero: every call writes what
+ * it reads. In debug mode the check result goes to the scratch too, where
+ * the caller cannot read it: debug with hstu_attn_fwd_cached. All calls on one GPU share its array, which keeps the last
+ * call's contents: calls that overlap on one GPU (different streams without
+ * ordering, or different host threads) race; order them on one stream.
+ */
+#define HSTU_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hstu_status_t hstu_attn_fwd_cached_noalloc(const hstu_params_t* params, int32_t batch,
+                                           const int32_t* new_offsets, const int32_t* cache_lens,
+                                           int32_t max_new, int32_t max_total, int64_t total_new,
+                                           const void* q_new, const void* u_new, const int64_t* ts_new,
+                                           const hstu_kv_cache_t* cache, void* y_new, hipStream_t stream);
 
 /*
  * M-FALCON candidate path. User b spans rows [history (n_b) | candidates

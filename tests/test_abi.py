@@ -185,6 +185,36 @@ def test_cached_and_mfalcon_and_append_reject_bad_arguments():
     assert r == WORKSPACE
 
 
+def test_noalloc_cached_rejects_before_touching_the_gpu():
+    # every case here returns before the scratch lookup (the first HIP call),
+    # so it is safe with fake pointers on any machine
+    lib = hs.lib()
+    c = hs._KVCache()
+    c.k_pages = c.v_pages = c.ts_pages = c.page_table = FAKE
+    c.num_pages, c.page_size, c.max_pages_per_seq = 1000, 64, 200
+    p = _params()
+    f = lib.hstu_attn_fwd_cached_noalloc
+    assert hs.HSTU_NOALLOC_SCRATCH_BYTES == 64 << 20
+    # the KV-delta serving shape fits: 8 users x 128 new, 8,320 keys, 4 x 128
+    need = lib.hstu_workspace_size(hs.HSTU_FN_CACHED, ctypes.byref(p), 8, 1024, 8320)
+    assert 0 < need <= hs.HSTU_NOALLOC_SCRATCH_BYTES
+    # 32,768 new tokens over 12,800 keys need more than the scratch holds
+    big = lib.hstu_workspace_size(hs.HSTU_FN_CACHED, ctypes.byref(p), 8, 32768, 12800)
+    assert big > hs.HSTU_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(p), 8, FAKE, FAKE, 4096, 12800, 32768, FAKE, FAKE, FAKE, ctypes.byref(c), FAKE,
+             None) == WORKSPACE
+    # argument checks as in hstu_attn_fwd_cached
+    assert f(ctypes.byref(p), 8, FAKE, None, 128, 8320, 1024, FAKE, FAKE, FAKE, ctypes.byref(c), FAKE,
+             None) == INVALID
+    assert f(ctypes.byref(p), 8, FAKE, FAKE, 128, 200 * 64 + 1, 1024, FAKE, FAKE, FAKE, ctypes.byref(c), FAKE,
+             None) == INVALID
+    c.page_size = 32
+    assert f(ctypes.byref(p), 8, FAKE, FAKE, 128, 8320, 1024, FAKE, FAKE, FAKE, ctypes.byref(c), FAKE,
+             None) == UNSUPPORTED
+    c.page_size = 64
+    assert f(ctypes.byref(p), 0, FAKE, FAKE, 128, 8320, 0, FAKE, FAKE, FAKE, ctypes.byref(c), FAKE, None) == OK
+
+
 def test_layer_workspace_and_bad_arguments_before_launch():
     lib = hs.lib()
     p = _params(num_heads=8)
