@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+FLOP_PER_CU_CYCLE_BF16 = 4096  # dense bf16 MFMA per CU per cycle (256 CUs x 2.4 GHz x 4096 = 2.5 PFLOP/s)
 PMC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_causal_B8_L8192_H4_d128_traffic.json")
 KERNEL_SOURCES = ("attn_fwd.hip", "tile.h", "common.h", "kernels.h")
 
@@ -59,12 +60,24 @@ def measured_traffic():
     return d.get("hbm_bytes_per_launch")
 
 
-def timed(fn, steps, warmup, torch, n_events=4):
-    """Run fn(events) warmup times, then `steps` timed times; returns
-    (ms per step over the whole region, list of per-step event tuples)."""
-    for _ in range(warmup):
+WARM = {"s": 0.25, "steps": 0}   # minimum warm-up time per timed region; last warm-up run (for the record)
+
+
+def timed(fn, steps, warmup, torch, n_events=4, warm_s=None):
+    """Run fn(events) at least `warmup` times and for at least warm_s seconds
+    of wall time (the GPU's clocks settle only after some continuous load),
+    then `steps` timed times; returns (ms per step over the whole region,
+    list of per-step event tuples)."""
+    warm_s = WARM["s"] if warm_s is None else warm_s
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < warm_s:
         fn(None)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    WARM["steps"], WARM["elapsed"] = n, time.perf_counter() - t0
     import hstu_jagged_silu_amd as hs
     evs = [[hs.HipEvent() for _ in range(n_events)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -75,6 +88,41 @@ def timed(fn, steps, warmup, torch, n_events=4):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps, evs
+
+
+def sustained_clock(torch, fn, samples=3):
+    """Shader clock (MHz) under the step's own load: the mean of amd-smi's
+    per-XCD gfx clocks, read `samples` times while fn runs back to back, and
+    the median of those reads. Returns (MHz, samples) or (None, reason)."""
+    import shutil
+    import subprocess
+    tool = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    reads = []
+    for _ in range(samples):
+        try:
+            pr = subprocess.Popen([tool, "metric", "-c", "--json"], stdout=subprocess.PIPE,
+                                  stderr=subprocess.DEVNULL, text=True)
+        except OSError as e:
+            return None, f"amd-smi not runnable: {e}"
+        n = 0
+        while pr.poll() is None:
+            fn(None)
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        try:
+            data = json.loads(pr.stdout.read())
+            gpus = data["gpu_data"] if isinstance(data, dict) else data
+            clk = gpus[0]["clock"]
+            mhz = [float(v["clk"]["value"]) for k, v in clk.items() if k.startswith("gfx_")]
+        except (ValueError, KeyError, IndexError, TypeError) as e:
+            return None, f"amd-smi output not parsed: {e}"
+        if not mhz or n == 0:
+            return None, "amd-smi returned no gfx clock"
+        reads.append(sum(mhz) / len(mhz))
+    reads.sort()
+    return reads[len(reads) // 2], [round(r, 1) for r in reads]
 
 
 def mean_span(evs, a, b):
@@ -187,6 +235,79 @@ def bench_cached(torch, hs, W, steps, warmup):
         "epilogue_ms": round(mean_span(evs, 2, 3), 4),
         "scheduler_ms": round(mean_span(evs, 0, 1), 4),
         "algorithmic_gflop": round(flop / 1e9, 3),
+    }
+
+
+def bench_kv_cache_8_layers(torch, hs, W, steps, warmup, layers=8):
+    """What the KV cache buys: an 8-layer serving step at batch 8 x (8,192
+    cached + 128 new tokens), per layer a paged append of the new tokens and
+    the cached forward, against recomputing the full causal path over the
+    8,320 tokens of every user at each of the 8 layers, on the same kernels.
+    Each layer has its own page pool and inputs (device copies of one drawn
+    layer), so no layer reads another's data from the caches."""
+    import numpy as np
+    ci = W.kv_cache_delta()
+    h = ci.hist
+    bf = torch.bfloat16
+    p = hs.LayerParams(num_heads=4, head_dim=128, dtype=bf, pos_tab=dev(torch, h.tables.pos),
+                       time_tab=dev(torch, h.tables.time))
+    table = dev(torch, ci.page_table)
+    base = hs.PagedKVCache.empty(ci.num_pages, 4, 128, table, dtype=bf)
+    pre, new = ci.split()
+    hs.hstu_kv_append(base, dev(torch, ci.prefix_offsets()), dev(torch, np.zeros(ci.batch, np.int32)),
+                      dev(torch, h.k[pre], bf), dev(torch, h.v[pre], bf), dev(torch, h.ts[pre]), p)
+    pools = [base] + [hs.PagedKVCache(base.k_pages.clone(), base.v_pages.clone(), base.ts_pages.clone(), table)
+                      for _ in range(layers - 1)]
+    new_rows = [tuple(dev(torch, x[new], bf) for x in (h.q, h.u, h.k, h.v)) for _ in range(1)]
+    new_rows += [tuple(t.clone() for t in new_rows[0]) for _ in range(layers - 1)]
+    tsn, noff, cl = dev(torch, h.ts[new]), dev(torch, ci.new_offsets()), dev(torch, ci.cache_lens)
+    max_total = int((ci.cache_lens + ci.new_lens).max())
+    max_new = int(ci.new_lens.max())
+    ys = [torch.empty_like(r[1]) for r in new_rows]
+    ws = torch.empty(hs.hstu_workspace_size(hs.HSTU_FN_CACHED, p, ci.batch, len(new), max_total),
+                     dtype=torch.uint8, device="cuda")
+
+    def cached_step(ev=None):
+        for pool, (qn, un, kn, vn), y in zip(pools, new_rows, ys):
+            hs.hstu_kv_append(pool, noff, cl, kn, vn, tsn, p)
+            hs.hstu_attn_fwd_cached(qn, un, tsn, noff, cl, max_new, max_total, pool, p, y=y, workspace=ws)
+
+    cached_ms, _ = timed(cached_step, steps, warmup, torch, n_events=0)
+    cached_graph_ms = graph_replay_ms(lambda: cached_step(None), steps, warmup, torch)
+
+    # the full causal path over the whole 8,320 tokens of every user, per layer
+    full_in = [tuple(dev(torch, x, bf) for x in (h.q, h.k, h.v, h.u))]
+    full_in += [tuple(t.clone() for t in full_in[0]) for _ in range(layers - 1)]
+    ts_all, off_all = dev(torch, h.ts), dev(torch, h.seq_offsets)
+    yf = [torch.empty_like(f[3]) for f in full_in]
+    wsf = torch.empty(hs.hstu_workspace_size(hs.HSTU_FN_FULL, p, ci.batch, h.total, h.max_len),
+                      dtype=torch.uint8, device="cuda")
+
+    def full_step(ev=None):
+        for (q, k, v, u), y in zip(full_in, yf):
+            hs.hstu_attn_fwd(q, k, v, u, ts_all, off_all, h.max_len, p, y=y, workspace=wsf)
+
+    full_ms, _ = timed(full_step, steps, warmup, torch, n_events=0)
+    full_graph_ms = graph_replay_ms(lambda: full_step(None), max(5, steps // 5), warmup, torch)
+    cached_flop = layers * 4 * 128 * 4 * hs.pair_count("cached", [int(x) for x in ci.new_lens],
+                                                       [int(x) for x in ci.cache_lens])
+    full_flop = layers * 4 * 128 * 4 * hs.pair_count("full", [int(x) for x in h.lengths])
+    del full_in, yf, wsf, pools, new_rows
+    return {
+        "workload": f"{layers} layers x {ci.name}",
+        "layers": layers,
+        "cached_step": "per layer: paged append of 128 new tokens per user + cached forward over 8,320 keys",
+        "full_step": "per layer: full causal forward over 8 users x 8,320 tokens",
+        "cached_ms_per_step": round(cached_ms, 4),
+        "cached_graph_ms_per_step": round(cached_graph_ms, 4),
+        "full_ms_per_step": round(full_ms, 4),
+        "full_graph_ms_per_step": round(full_graph_ms, 4),
+        "latency_ratio_full_over_cached": round(full_ms / cached_ms, 2),
+        "latency_ratio_graphs": round(full_graph_ms / cached_graph_ms, 2),
+        "cached_algorithmic_gflop": round(cached_flop / 1e9, 3),
+        "full_algorithmic_gflop": round(full_flop / 1e9, 3),
+        "pages_context": "the pages report a 5.93x latency reduction for an 8-layer model at this shape with every "
+                         "history cached, on other hardware and against their own full path (context, not a target)",
     }
 
 
@@ -491,6 +612,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup-seconds", type=float, default=1.5,
+                    help="warm up the headline step for at least this long (on top of --warmup steps)")
+    ap.add_argument("--variant-warmup-seconds", type=float, default=0.3)
     ap.add_argument("--no-variants", action="store_true", help="time only the headline workload")
     ap.add_argument("--variants", default="", help="comma-separated subset of the variants to run (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -515,7 +639,10 @@ def main():
         sys.exit(1)
 
     log("headline: 8 x 8192, 4 x 128, bf16")
+    WARM["s"] = args.warmup_seconds
     inp, ms, evs, flop, step_fn = bench_full(torch, hs, W, args.steps, args.warmup)
+    warm_steps, warm_elapsed = WARM["steps"], WARM["elapsed"]
+    WARM["s"] = args.variant_warmup_seconds
     attn_ms = mean_span(evs, 1, 2)
     attn_each = sorted(e[1].elapsed_ms(e[2]) for e in evs)
     attn_median = attn_each[len(attn_each) // 2]
@@ -529,6 +656,21 @@ def main():
     log(f"step {ms:.4f} ms ({value:.1f} TFLOP/s), attention kernel {attn_ms:.4f} ms ({achieved:.1f} TFLOP/s), "
         f"scheduler {sched_ms:.4f} ms, epilogue {ln_ms:.4f} ms")
 
+    clock_mhz, clock_reads = sustained_clock(torch, step_fn)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    peak_sustained = None
+    if clock_mhz is not None:
+        # 32x32x16 bf16 MFMA: 32,768 FLOP per 32 cycles per SIMD, 4 SIMDs per CU
+        sus = cus * clock_mhz * 1e6 * FLOP_PER_CU_CYCLE_BF16 / 1e12
+        peak_sustained = {"value": round(sus, 1), "unit": "TFLOP/s", "cus": cus, "clock_mhz": round(clock_mhz, 1),
+                          "flop_per_cu_cycle": FLOP_PER_CU_CYCLE_BF16, "frac": round(achieved / sus, 4),
+                          "clock_reads_mhz": clock_reads,
+                          "source": "amd-smi metric -c: mean of the per-XCD gfx clocks, median of 3 reads "
+                                    "taken while the headline step ran back to back"}
+        log(f"sustained clock {clock_mhz:.0f} MHz -> peak {sus:.0f} TFLOP/s, attention at {achieved / sus:.3f}")
+    else:
+        log(f"sustained clock not measured: {clock_reads}")
+
     result = {
         "metric": "HSTU attention TFLOP/s + % bf16 MFMA peak (1 GPU); ms/layer at seq 8192, d=128",
         "value": round(value, 2),
@@ -536,6 +678,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": {"steps": warm_steps, "seconds": round(warm_elapsed, 3), "min_seconds": args.warmup_seconds},
         "ms_per_step": round(ms, 4),
         "ms_per_layer": round(ms, 4),
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
@@ -552,6 +695,7 @@ def main():
                      "kernel": "attn_fwd_kernel<bf16,128,full>", "kernel_ms": round(attn_ms, 4),
                      "kernel_ms_median": round(attn_median, 4),
                      "kernel_ms_cold_median": round(cold[len(cold) // 2], 4)},
+        "peak_sustained": peak_sustained,
         "kernels_ms": {"scheduler": round(sched_ms, 4), "attention": round(attn_ms, 4),
                        "ln_gate": round(ln_ms, 4)},
         "epilogue": {"bound": "hbm", "achieved_gbs": round(ln_bytes / (ln_ms * 1e-3) / 1e9, 1),
@@ -572,7 +716,8 @@ def main():
         del src, dst, flush
     if not args.no_variants:
         variants = {}
-        for name, fn in (("kv_cache_delta", bench_cached), ("mfalcon", bench_mfalcon),
+        for name, fn in (("kv_cache_delta", bench_cached), ("kv_cache_8_layers", bench_kv_cache_8_layers),
+                         ("mfalcon", bench_mfalcon),
                          ("mfalcon_paged_history", bench_mfalcon_paged),
                          ("jagged_training_shape", bench_training_shape), ("full_layer", bench_layer),
                          ("full_layer_own_products",

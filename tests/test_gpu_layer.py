@@ -47,16 +47,19 @@ def test_layer_head_dim_64_and_empty_user():
 
 @pytest.mark.parametrize("products", PRODUCTS)
 def test_full_size_layer_sampled_rows(products):
-    """Batch 16, lognormal lengths (median 2,048) capped at 8,192, E = 1,024, 8 x 128: sampled rows."""
+    """Batch 16, lognormal lengths (median 2,048) capped at 8,192, E = 1,024, 8 x 128: sampled rows,
+    from the shortest users and from the longest."""
     inp = W.full_layer()
     y = run_layer(inp, products=products)
     assert np.isfinite(y).all()
     off = inp.seq_offsets
     rng = np.random.default_rng(11)
-    # rows from the three shortest non-empty users plus the first and last row of
-    # the whole batch; the oracle recomputes f1 for each sampled user's prefix
+    # rows from the three shortest non-empty users and the two longest (8,192
+    # tokens: the last query tile, every key tile) plus the first and last row
+    # of the whole batch; the oracle recomputes f1 for each sampled user's prefix
     lens = np.diff(off)
-    users = [b for b in np.argsort(lens) if lens[b] > 0][:3]
+    order = [b for b in np.argsort(lens, kind="stable") if lens[b] > 0]
+    users = order[:3] + order[-2:]
     rows = [0, int(off[-1]) - 1]
     for b in users:
         s0, s1 = int(off[b]), int(off[b + 1])

@@ -116,6 +116,25 @@ def test_long_sequences_sampled_rows():
     assert np.isfinite(y).all()
 
 
+def test_long_sequences_one_whole_user():
+    """8 users x 8,192 tokens, 4 x 128, bf16 (the benchmark's workload, in the
+    benchmark's launch): every row and head of the last user against the
+    oracle run on that user alone (users are independent: a jagged batch
+    equals per-user runs)."""
+    inp = W.long_seq()
+    y = to_np(run_full(inp))
+    b = len(inp.seq_offsets) - 2
+    s0, s1 = int(inp.seq_offsets[b]), int(inp.seq_offsets[b + 1])
+    assert s1 - s0 == 8192
+    print(f"user {b}: rows {s0} .. {s1 - 1}, running the oracle on the whole user", flush=True)
+    y_ref, _ = oracle.hstu_full(inp.q[s0:s1], inp.k[s0:s1], inp.v[s0:s1], inp.u[s0:s1], inp.ts[s0:s1],
+                                np.array([0, s1 - s0]), inp.tables.pos, inp.tables.time)
+    err = oracle.max_rel_row_error(y[s0:s1], y_ref)
+    print(f"8x8192 whole user {b} (8,192 rows x 4 heads) max row rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    assert np.isfinite(y).all()
+
+
 def test_more_than_4096_items_sampled_rows():
     """64 users x 8 heads: 4,608 work items, more than the scheduler keeps in
     registers between its histogram and scatter passes (the rest are rebuilt)."""
