@@ -150,13 +150,13 @@ def dev(torch, x, dt=None):
     return (t.to(dt) if dt is not None else t).cuda()
 
 
-def bench_full(torch, hs, W, steps, warmup):
+def bench_full(torch, hs, W, steps, warmup, flags=0):
     inp = W.long_seq()
     bf = torch.bfloat16
     q, k, v, u = (dev(torch, x, bf) for x in (inp.q, inp.k, inp.v, inp.u))
     ts, off = dev(torch, inp.ts), dev(torch, inp.seq_offsets)
     p = hs.LayerParams(num_heads=4, head_dim=128, dtype=bf, pos_tab=dev(torch, inp.tables.pos),
-                       time_tab=dev(torch, inp.tables.time))
+                       time_tab=dev(torch, inp.tables.time), flags=flags)
     y = torch.empty_like(u)
     ws = torch.empty(hs.hstu_workspace_size(hs.HSTU_FN_FULL, p, inp.batch, inp.total, inp.max_len),
                      dtype=torch.uint8, device="cuda")
@@ -652,7 +652,8 @@ def main():
     value = flop / (ms * 1e-3) / 1e12
     achieved = flop / (attn_ms * 1e-3) / 1e12
     hd = 4 * 128
-    ln_bytes = inp.total * hd * (4 + 2 + 2)   # O fp32 read, U read, Y write (bf16)
+    # norm-ready store: bf16 deviations + 8 bytes per (token, head) read, U read, Y written (bf16)
+    ln_bytes = inp.total * hd * (2 + 2 + 2) + inp.total * 4 * 8
     log(f"step {ms:.4f} ms ({value:.1f} TFLOP/s), attention kernel {attn_ms:.4f} ms ({achieved:.1f} TFLOP/s), "
         f"scheduler {sched_ms:.4f} ms, epilogue {ln_ms:.4f} ms")
 
@@ -701,6 +702,20 @@ def main():
         "epilogue": {"bound": "hbm", "achieved_gbs": round(ln_bytes / (ln_ms * 1e-3) / 1e9, 1),
                      "peak_gbs": PEAK_HBM_GBS, "bytes": ln_bytes},
     }
+    if not args.no_variants:
+        # the same step with the attention output making an fp32 round trip to
+        # the norm (the path before the norm-ready store)
+        _, ms32, evs32, _, _ = bench_full(torch, hs, W, args.steps, args.warmup, flags=hs.HSTU_FLAG_FP32_NORM_INPUT)
+        result["norm_input"] = {
+            "norm_ready_store": {"ms_per_step": round(ms, 4), "attention_ms": round(attn_ms, 4),
+                                 "norm_ms": round(ln_ms, 4),
+                                 "attention_output_bytes": inp.total * hd * 2 + inp.total * 4 * 8},
+            "fp32_round_trip": {"ms_per_step": round(ms32, 4), "attention_ms": round(mean_span(evs32, 1, 2), 4),
+                                "norm_ms": round(mean_span(evs32, 2, 3), 4),
+                                "attention_output_bytes": inp.total * hd * 4},
+        }
+        log(f"fp32 norm input: step {ms32:.4f} ms, attention {mean_span(evs32, 1, 2):.4f} ms, "
+            f"norm {mean_span(evs32, 2, 3):.4f} ms")
     if args.copy_calibration_mib > 0:
         # a plain device-to-device copy of n bytes; a 1 GiB write in between
         # evicts the source from L2 and the 256 MB Infinity Cache first

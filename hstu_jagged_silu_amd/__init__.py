@@ -29,6 +29,7 @@ LIB_PATH = os.path.join(_PKG, "libhstu.so")
 HSTU_F32, HSTU_BF16 = 0, 1
 HSTU_FN_FULL, HSTU_FN_CACHED, HSTU_FN_MFALCON, HSTU_FN_MFALCON_CACHED, HSTU_FN_FULL_BWD = 0, 1, 2, 3, 4
 PAGE_SIZE = 64
+HSTU_FLAG_FP32_NORM_INPUT = 1
 
 EXPORTED_SYMBOLS = (
     "hstu_status_string", "hstu_version", "hstu_workspace_size", "hstu_attn_fwd",
@@ -51,7 +52,7 @@ class _Params(ctypes.Structure):
         ("pos_tab", ctypes.c_void_p), ("n_pos", ctypes.c_int32), ("pos_head_stride", ctypes.c_int32),
         ("time_tab", ctypes.c_void_p), ("n_time", ctypes.c_int32), ("time_head_stride", ctypes.c_int32),
         ("ln_w", ctypes.c_void_p), ("ln_b", ctypes.c_void_p), ("ln_eps", ctypes.c_float),
-        ("timing_events", ctypes.c_void_p * 4),
+        ("timing_events", ctypes.c_void_p * 4), ("flags", ctypes.c_int32),
     ]
 
 
@@ -168,6 +169,7 @@ class LayerParams:
     ln_w: Optional[torch.Tensor] = None
     ln_b: Optional[torch.Tensor] = None
     ln_eps: float = 1e-5
+    flags: int = 0   # HSTU_FLAG_FP32_NORM_INPUT: fp32 attention output round trip instead of the norm-ready store
 
     def c_struct(self, timing_events=None) -> _Params:
         p = _Params()
@@ -203,6 +205,7 @@ class LayerParams:
                     raise ValueError(f"{name} must have H*d elements")
             setattr(p, name, None if t is None else t.data_ptr())
         p.ln_eps = self.ln_eps
+        p.flags = self.flags
         if timing_events is not None:
             for i, ev in enumerate(timing_events[:4]):
                 p.timing_events[i] = None if ev is None else ev.cuda_event

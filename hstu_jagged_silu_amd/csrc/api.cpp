@@ -70,6 +70,7 @@ hstu_status_t check_params(const hstu_params_t* p) {
     if (p->time_head_stride != 0 && p->time_head_stride < p->n_time) return HSTU_ERR_INVALID_ARG;
   }
   if ((p->ln_w && !aligned16(p->ln_w)) || (p->ln_b && !aligned16(p->ln_b))) return HSTU_ERR_INVALID_ARG;
+  if (p->flags & ~HSTU_FLAG_FP32_NORM_INPUT) return HSTU_ERR_INVALID_ARG;
   return HSTU_OK;
 }
 
@@ -171,6 +172,23 @@ SchedArgs sched_args(int mode, const hstu_params_t* p, const WsLayout& w, void* 
   // ranges are only needed when a time table is present
   s.n_stat_blocks = p->time_tab ? w.n_stat_blocks : 0;
   return s;
+}
+
+// bf16 paths with one key split hand the norm a norm-ready store (bf16
+// deviations from each head's mean, then the heads' (mean, M2) pairs) in the
+// space of the fp32 O buffer, unless the caller asks for the fp32 round trip.
+// T * H * d * 2 bytes of deviations keep the pairs 64-byte aligned, and
+// 2 + 8 / d <= 4 bytes per element fit in the fp32 buffer.
+void norm_ready(const hstu_params_t* p, const WsLayout& w, void* ws, int64_t T, AttnArgs& a, LnArgs& l) {
+  if (p->dtype != HSTU_BF16 || w.n_chunks != 1 || (p->flags & HSTU_FLAG_FP32_NORM_INPUT)) return;
+  const int64_t HD = (int64_t)p->num_heads * p->head_dim;
+  bf16* dev = (bf16*)((char*)ws + w.o_off);
+  float* stats = (float*)((char*)ws + w.o_off + (size_t)T * (size_t)HD * 2);
+  a.o_dev = dev;
+  l.o_dev = dev;
+  a.o_stats = stats;
+  l.o_stats = stats;
+  l.head_dim = p->head_dim;
 }
 
 LnArgs ln_args(const hstu_params_t* p, const WsLayout& w, void* ws, const void* u, void* y, int64_t T) {
@@ -294,6 +312,7 @@ hstu_status_t hstu_attn_fwd(const hstu_params_t* params, int32_t batch, const in
   a.ts = ts;
   a.offsets = seq_offsets;
   LnArgs l = ln_args(params, w, ws, u, y, total_tokens);
+  norm_ready(params, w, ws, total_tokens, a, l);
   if (!debug_check(rows_check(batch, seq_offsets, total_tokens, max_len), ws, s, stream)) return HSTU_ERR_LAUNCH;
   return run_attention(params, s, a, MODE_FULL, l, stream);
 }
@@ -437,6 +456,7 @@ hstu_status_t hstu_mfalcon_fwd(const hstu_params_t* params, int32_t batch, const
   a.offsets = seq_offsets;
   a.num_cand = num_candidates;
   LnArgs l = ln_args(params, w, ws, u, y, total_tokens);
+  norm_ready(params, w, ws, total_tokens, a, l);
   ValidateArgs chk = rows_check(batch, seq_offsets, total_tokens, max_len);
   chk.num_cand = num_candidates;
   if (!debug_check(chk, ws, s, stream)) return HSTU_ERR_LAUNCH;

@@ -510,6 +510,65 @@ void attn_fwd_kernel(AttnArgs a) {
   // (each holds 64 rows of D fp32 values); chunks are XOR-swizzled by row.
   __syncthreads();  // every wave is done reading the stages
   const float oscale = -LN2 / (float)n_norm;
+  if constexpr (sizeof(T) == 2 && (MODE == MODE_FULL || MODE == MODE_MFALCON)) {
+    if (a.o_dev != nullptr) {
+      // Norm-ready store. This lane holds half of its row's D values (the
+      // other half is in lane ^ 32). The head's mean and sum of squared
+      // deviations come from the fp32 values (two passes over registers);
+      // the deviations go out as bf16, so their rounding is relative to the
+      // head's spread, not to a common offset of the row.
+      float sum = 0.0f;
+      #pragma unroll
+      for (int db = 0; db < G::NDB; ++db) {
+        #pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          oacc[db][v] *= oscale;
+          sum += oacc[db][v];
+        }
+      }
+      sum += __shfl_xor(sum, 32);
+      const float mean_h = sum * (1.0f / (float)D);
+      float m2 = 0.0f;
+      #pragma unroll
+      for (int db = 0; db < G::NDB; ++db) {
+        #pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          oacc[db][v] -= mean_h;
+          m2 = fmaf(oacc[db][v], oacc[db][v], m2);
+        }
+      }
+      m2 += __shfl_xor(m2, 32);
+      const int64_t grow = q_off + q_start + row_w;
+      if (hl == 0 && row_ok && grow < a.Tq)
+        *(f32x2*)(a.o_stats + 2 * (grow * H + h)) = f32x2{mean_h, m2};
+      // bf16 rows staged in stage 0's memory (128 rows x D x 2 bytes)
+      constexpr int BCPR = D / 8;  // 16-byte chunks (8 values) per bf16 row
+      static_assert(sizeof(Stage<T, D>) >= QT * D * 2, "bf16 output staging fits one stage");
+      auto bstage = [&](int r) { return (bf16*)(unsigned char*)&st0 + r * D; };
+      #pragma unroll
+      for (int db = 0; db < G::NDB; ++db) {
+        #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          // values d = 32 db + 8 g + 4 hl + (0..3): half of a 16-byte chunk
+          const int d0 = 32 * db + 8 * g + 4 * hl;
+          bf16x4 x;
+          #pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = (bf16)oacc[db][4 * g + e];
+          const int c = d0 / 8;
+          *(bf16x4*)(bstage(row_w) + (c ^ (row_w % BCPR)) * 8 + (d0 % 8)) = x;
+        }
+      }
+      __syncthreads();
+      for (int i = tid; i < QT * BCPR; i += NTHREADS) {
+        const int r = i / BCPR, c = i % BCPR;
+        if (r < q_len && q_off + q_start + r < a.Tq) {
+          const bf16x8 x = *(const bf16x8*)(bstage(r) + (c ^ (r % BCPR)) * 8);
+          *(bf16x8*)(a.o_dev + ((q_off + q_start + r) * H + h) * D + c * 8) = x;
+        }
+      }
+      return;
+    }
+  }
   constexpr int OCPR = D / 4;  // 16-byte chunks per output row
   static_assert(sizeof(Stage<T, D>) >= 64 * D * 4, "output staging fits one stage per 64 rows");
   auto ostage = [&](int r) { return (float*)(r < 64 ? (unsigned char*)&st0 : (unsigned char*)&st1) + (r & 63) * D; };

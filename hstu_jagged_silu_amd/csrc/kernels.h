@@ -32,6 +32,12 @@ struct AttnArgs {
   float* o;                      // [n_chunks][Tq][H*D] fp32, scaled attention output
   int64_t o_chunk_stride;        // elements between key splits
   int32_t n_chunks;              // key splits the O buffer holds
+  // Norm-ready store (bf16, one key split): when o_dev is set, the kernel
+  // writes, instead of o, each (row, head)'s deviations from its head mean
+  // as bf16 [Tq][H*D] and the head's (mean, sum of squared deviations) as
+  // float2 [Tq][H], both from the fp32 accumulators
+  bf16* o_dev;
+  float* o_stats;
   // key timestamp range per 64-key block: jagged variants index packed rows
   // (block i = rows [64i, 64i + 64)), the cached path indexes [b][key tile]
   const int64_t* tstats;         // pairs (min, max)
@@ -66,6 +72,11 @@ struct SchedArgs {
 // Arguments of the LayerNorm + U gating epilogue (sums key splits first).
 struct LnArgs {
   const float* o;                // [n_chunks][T][HD]
+  // norm-ready input (instead of o): bf16 deviations [T][HD] and per-head
+  // (mean, sum of squared deviations) [T][H] with heads of head_dim values
+  const bf16* o_dev;
+  const float* o_stats;
+  int32_t head_dim;
   int64_t o_chunk_stride;
   const void* u;                 // [T, HD]
   void* y;                       // [T, HD]

@@ -7,7 +7,9 @@
 // One wave64 per token row. Every global access is a contiguous row segment
 // (16 bytes of O per lane, 8 or 16 bytes of U and Y), and all loads of a row
 // are issued before the first reduction so that they overlap. HBM-bound: per
-// element it reads 4 bytes of O per split plus U and writes Y.
+// element it reads 4 bytes of O per split plus U and writes Y. A second form
+// finishes the attention kernel's norm-ready store (bf16 deviations and
+// per-head statistics) with 2 bytes of O per element.
 #include "kernels.h"
 
 namespace hstu {
@@ -152,6 +154,78 @@ __global__ __launch_bounds__(64 * LN_ROWS) void ln_gate_kernel(LnArgs a) {
   }
 }
 
+// The same norm and gating from the attention kernel's norm-ready store: per
+// row, H (mean_h, M2_h) pairs over head_dim values each and the bf16
+// deviations o - mean_h. The pairs merge exactly (Chan et al.'s pairwise
+// update with equal counts): mean = average of mean_h, and
+// M2 = sum M2_h + head_dim * sum (mean_h - mean)^2. Then
+// y = ((dev + mean_h - mean) / sqrt(M2 / HD + eps) * w + b) * u.
+// Reads 2 bytes of deviation per element (and 8 bytes per head) instead of
+// 4 bytes of O.
+template <int NCH, bool FULL_LANES>
+__global__ __launch_bounds__(64 * LN_ROWS) void ln_gate_dev_kernel(LnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * LN_ROWS + (threadIdx.x >> 6);
+  if (row >= a.T) return;
+  const int nch = a.HD / 4;
+  const int H = a.HD / a.head_dim;
+
+  bool on[NCH];
+  int col[NCH];
+  #pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    on[i] = FULL_LANES || c < nch;
+    col[i] = 4 * (FULL_LANES ? c : min(c, nch - 1));
+  }
+  const bf16* drow = a.o_dev + row * a.HD;
+  const bf16* urow = (const bf16*)a.u + row * a.HD;
+  const float* srow = a.o_stats + 2 * row * H;
+  f32x4 z[NCH], u[NCH];
+  #pragma unroll
+  for (int i = 0; i < NCH; ++i) z[i] = load4(drow + col[i]);
+  #pragma unroll
+  for (int i = 0; i < NCH; ++i) u[i] = load4(urow + col[i]);
+  float mh[NCH];
+  #pragma unroll
+  for (int i = 0; i < NCH; ++i) mh[i] = srow[2 * (col[i] / a.head_dim)];
+
+  // merge the heads' statistics (H <= 64: one head per lane)
+  const f32x2 st = lane < H ? *(const f32x2*)(srow + 2 * lane) : f32x2{0.0f, 0.0f};
+  const float mean = wave_sum(st[0]) / (float)H;
+  const float dm = lane < H ? st[0] - mean : 0.0f;
+  const float m2 = wave_sum(fmaf((float)a.head_dim * dm, dm, st[1]));
+  const float rstd = rsqrtf(m2 / (float)a.HD + a.eps);
+  bf16* yrow = (bf16*)a.y + row * a.HD;
+  #pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    if (!on[i]) continue;
+    f32x4 w = {1, 1, 1, 1}, bb = {0, 0, 0, 0};
+    if (a.ln_w) w = *(const f32x4*)(a.ln_w + col[i]);
+    if (a.ln_b) bb = *(const f32x4*)(a.ln_b + col[i]);
+    const float shift = mh[i] - mean;
+    f32x4 yv;
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) yv[e] = fmaf((z[i][e] + shift) * rstd, w[e], bb[e]) * u[i][e];
+    store4(yrow + col[i], yv);
+  }
+}
+
+static void launch_dev(const LnArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div(a.T, LN_ROWS)), blk(64 * LN_ROWS);
+  switch (a.HD) {
+    case 256: hipLaunchKernelGGL((ln_gate_dev_kernel<1, true>), grid, blk, 0, s, a); return;
+    case 512: hipLaunchKernelGGL((ln_gate_dev_kernel<2, true>), grid, blk, 0, s, a); return;
+    case 1024: hipLaunchKernelGGL((ln_gate_dev_kernel<4, true>), grid, blk, 0, s, a); return;
+    case 2048: hipLaunchKernelGGL((ln_gate_dev_kernel<8, true>), grid, blk, 0, s, a); return;
+  }
+  const int nch = (int)ceil_div(a.HD / 4, 64);
+  if (nch <= 1) hipLaunchKernelGGL((ln_gate_dev_kernel<1, false>), grid, blk, 0, s, a);
+  else if (nch <= 2) hipLaunchKernelGGL((ln_gate_dev_kernel<2, false>), grid, blk, 0, s, a);
+  else if (nch <= 4) hipLaunchKernelGGL((ln_gate_dev_kernel<4, false>), grid, blk, 0, s, a);
+  else hipLaunchKernelGGL((ln_gate_dev_kernel<8, false>), grid, blk, 0, s, a);
+}
+
 template <typename T>
 static void launch_t(const LnArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div(a.T, LN_ROWS)), blk(64 * LN_ROWS);
@@ -170,7 +244,10 @@ static void launch_t(const LnArgs& a, hipStream_t s) {
 
 hipError_t launch_ln_gate(const LnArgs& a, int dtype, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  if (dtype == 1) launch_t<bf16>(a, s);
+  if (a.o_dev != nullptr) {
+    if (dtype != 1 || a.head_dim < 4 || a.HD % a.head_dim != 0 || a.HD / a.head_dim > 64) return hipErrorInvalidValue;
+    launch_dev(a, s);
+  } else if (dtype == 1) launch_t<bf16>(a, s);
   else launch_t<float>(a, s);
   return hipGetLastError();
 }

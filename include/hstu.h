@@ -123,6 +123,18 @@ typedef enum {
  *                 [1] before the fused attention kernel, [2] after it, [3]
  *                 after the LayerNorm/gating epilogue. For timing the kernels
  *                 of one call separately; the library never waits on them.
+ *   flags         0, or HSTU_FLAG_FP32_NORM_INPUT. How the attention kernel
+ *                 hands its output to the norm on the bf16 full and M-FALCON
+ *                 paths: by default the attention store is norm-ready (per
+ *                 token and head, the mean and the sum of squared deviations
+ *                 of the head's d values, computed from the fp32
+ *                 accumulators, plus the deviations rounded to bf16), and the
+ *                 norm kernel only merges the heads' statistics and applies
+ *                 the affine terms and U. With the flag the attention output
+ *                 makes an fp32 round trip instead (twice the bytes); the two
+ *                 agree within bf16 rounding of the deviations. fp32 layers,
+ *                 the split paged paths and the backward always use fp32.
+ *                 Other bits: HSTU_ERR_INVALID_ARG.
  */
 typedef struct {
   int32_t num_heads;
@@ -140,7 +152,11 @@ typedef struct {
   const float* ln_b;
   float ln_eps;
   void* timing_events[4];
+  int32_t flags;
 } hstu_params_t;
+
+/* hstu_params_t.flags bits */
+#define HSTU_FLAG_FP32_NORM_INPUT 1
 
 /*
  * Paged KV cache ("paged GPU table", page "recomendador-generativo-hstu-

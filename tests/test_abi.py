@@ -52,6 +52,7 @@ int main(void) {
   P(hstu_params_t, norm_n); P(hstu_params_t, pos_tab); P(hstu_params_t, n_pos); P(hstu_params_t, pos_head_stride);
   P(hstu_params_t, time_tab); P(hstu_params_t, n_time); P(hstu_params_t, time_head_stride);
   P(hstu_params_t, ln_w); P(hstu_params_t, ln_b); P(hstu_params_t, ln_eps); P(hstu_params_t, timing_events);
+  P(hstu_params_t, flags);
   printf("hstu_kv_cache_t %zu\n", sizeof(hstu_kv_cache_t));
   P(hstu_kv_cache_t, k_pages); P(hstu_kv_cache_t, v_pages); P(hstu_kv_cache_t, ts_pages);
   P(hstu_kv_cache_t, page_table); P(hstu_kv_cache_t, num_pages); P(hstu_kv_cache_t, page_size);
@@ -125,6 +126,8 @@ def test_workspace_size_valid_and_invalid():
     assert _ws(0, _params(num_heads=0), 8, 1024, 128) == 0
     assert _ws(0, p, -1, 1024, 128) == 0
     assert _ws(0, _params(ln_eps=0.0), 8, 1024, 128) == 0
+    assert _ws(0, _params(flags=hs.HSTU_FLAG_FP32_NORM_INPUT), 8, 65536, 8192) == full  # same workspace
+    assert _ws(0, _params(flags=2), 8, 1024, 128) == 0          # unknown flag bit
 
 
 FAKE = 0x10000  # aligned, never dereferenced: validation fails before any launch

@@ -324,3 +324,68 @@ def test_mfalcon_candidates_independent_bitwise():
     inp.v[other] = 0
     y2 = to_np(_run_mfalcon(ci))
     assert np.array_equal(y[:357], y2[:357])
+
+
+# ---------------------------------------------------------------- norm input
+
+FP32_IN = 1  # HSTU_FLAG_FP32_NORM_INPUT
+
+
+def _both_norm_inputs(inp, ref, label, **pkw):
+    """The bf16 full path with the norm-ready store (default) and with the fp32
+    round trip, each against the oracle, and against each other."""
+    ys = []
+    for flags in (0, FP32_IN):
+        p = params_for(inp.dtype, inp.num_heads, inp.head_dim, inp.tables, flags=flags, **pkw)
+        ys.append(to_np(run_full(inp, p)))
+        err = oracle.max_rel_row_error(ys[-1], ref)
+        print(f"{label} flags={flags}: max row rel err {err:.3e}", flush=True)
+        assert err <= TOL["bf16"]
+    assert oracle.max_rel_row_error(ys[0], ys[1]) <= TOL["bf16"]
+    return ys
+
+
+@pytest.mark.parametrize("d", [128, 64, 32])
+def test_norm_ready_store_ragged_all_head_dims(d):
+    inp = W.jagged(f"normready_d{d}", 401, [1, 77, 200, 130, 0, 64, 129, 300], 4, d, "bf16", 128, 128)
+    _both_norm_inputs(inp, oracle_full(inp), f"norm-ready d={d}")
+
+
+def test_norm_ready_store_training_shape_and_affine():
+    inp = W.training_shape()
+    w, b = W.affine_terms(402, 512)
+    ref, _ = oracle.hstu_full(inp.q, inp.k, inp.v, inp.u, inp.ts, inp.seq_offsets, inp.tables.pos,
+                              inp.tables.time, gamma=w, beta=b)
+    _both_norm_inputs(inp, ref, "training shape + affine", ln_w=dev(w), ln_b=dev(b))
+
+
+def test_norm_ready_store_sixteen_heads():
+    # H * d = 2,048: the finisher merges 16 heads' statistics per row
+    inp = W.jagged("normready_h16", 403, [700, 45, 300], 16, 128, "bf16", 256, 64)
+    _both_norm_inputs(inp, oracle_full(inp), "16 heads")
+
+
+def test_norm_ready_store_large_common_offset():
+    """V = N(0, 1) + 40 with one head: every output row is a large common
+    offset plus a small spread. The store keeps deviations from the head's
+    mean, so bf16 rounding stays relative to the spread (a bf16 copy of O
+    itself would lose the spread to rounding of the offset, about 40 x 2^-9
+    of the row sum against a spread of the row sum over sqrt(keys)). One head,
+    because the bf16 P of each head scales the offset by its own rounding
+    error, which the norm removes only when the row is one head."""
+    inp = W.jagged("normready_offset", 404, [150, 400, 64], 1, 128, "bf16", 128, 128)
+    inp.v = W.round_to_bf16((inp.v + 40.0).astype(np.float32))
+    _both_norm_inputs(inp, oracle_full(inp), "common offset 40")
+
+
+def test_norm_ready_store_mfalcon():
+    ci = W.candidates("normready_mf", 405, [300, 0, 129], [50, 7, 64])
+    ref = _oracle_mfalcon(ci)
+    inp = ci.inputs
+    ys = []
+    for flags in (0, FP32_IN):
+        ys.append(to_np(_run_mfalcon(ci, params_for(inp.dtype, inp.num_heads, inp.head_dim, inp.tables,
+                                                     flags=flags))))
+        err = oracle.max_rel_row_error(ys[-1], ref)
+        print(f"M-FALCON flags={flags}: max row rel err {err:.3e}", flush=True)
+        assert err <= TOL["bf16"]
