@@ -589,10 +589,14 @@ def max_rel_row_error(y, y_ref, zero_row_atol=1e-6):
     whose reference is identically zero must instead satisfy
     ||y_t||_inf <= zero_row_atol (reported as inf otherwise).
     """
-    y = np.asarray(y, dtype=np.float64).reshape(len(y_ref), -1)
-    y_ref = np.asarray(y_ref, dtype=np.float64).reshape(len(y_ref), -1)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
     if y_ref.size == 0:
+        if y.size != 0:
+            raise ValueError("output has values where the reference has none")
         return 0.0
+    y = y.reshape(len(y_ref), -1)
+    y_ref = y_ref.reshape(len(y_ref), -1)
     num = np.abs(y - y_ref).max(axis=1)
     den = np.abs(y_ref).max(axis=1)
     zero = den == 0

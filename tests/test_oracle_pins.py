@@ -426,6 +426,10 @@ def test_max_rel_row_error():
     assert oracle.max_rel_row_error(ref, ref) == 0.0
     assert oracle.max_rel_row_error(ref + [[0.02, 0], [0, 0]], ref) == pytest.approx(0.01)
     assert oracle.max_rel_row_error(ref + [[0, 0], [0, 1e-3]], ref) == float("inf")
+    # no rows at all (a batch whose users have no new tokens)
+    assert oracle.max_rel_row_error(np.zeros((0, 4)), np.zeros((0, 4))) == 0.0
+    with pytest.raises(ValueError):
+        oracle.max_rel_row_error(np.zeros((1, 4)), np.zeros((0, 4)))
 
 
 def test_max_err_vs_scale_hand_computed():
