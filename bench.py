@@ -475,7 +475,7 @@ def bench_layer(torch, hs, W, steps, warmup, products=0):
     f1_ms, attn_ms, f2_ms = mean_span(evs, 0, 1), mean_span(evs, 1, 2), mean_span(evs, 2, 3)
     return {
         "workload": inp.name,
-        "products": "own MFMA kernel" if products else "hipBLASLt",
+        "products": {0: "hipBLASLt", 1: "own MFMA kernel", 2: "own f1 (fused SiLU/split) + hipBLASLt f2"}[products],
         "total_tokens": T,
         "ms_per_step": round(ms, 4),
         "tflops": round((f1_flop + f2_flop + attn_flop) / (ms * 1e-3) / 1e12, 2),
@@ -737,6 +737,8 @@ def main():
                          ("jagged_training_shape", bench_training_shape), ("full_layer", bench_layer),
                          ("full_layer_own_products",
                           lambda torch, hs, W, st, wu: bench_layer(torch, hs, W, st, wu, products=1)),
+                         ("full_layer_auto_products",
+                          lambda torch, hs, W, st, wu: bench_layer(torch, hs, W, st, wu, products=2)),
                          ("backward_training_shape", bench_backward_training),
                          ("backward_causal_B8_L8192", bench_backward_long)):
             if args.variants and name not in args.variants.split(","):

@@ -75,7 +75,7 @@ class _LayerWeights(ctypes.Structure):
                 ("products", ctypes.c_int32)]
 
 
-HSTU_PRODUCTS_HIPBLASLT, HSTU_PRODUCTS_OWN = 0, 1
+HSTU_PRODUCTS_HIPBLASLT, HSTU_PRODUCTS_OWN, HSTU_PRODUCTS_AUTO = 0, 1, 2
 
 
 def _load():
@@ -375,12 +375,13 @@ def hstu_layer_workspace_size(params: LayerParams, embed_dim: int, batch: int, t
 
 
 def hstu_layer_fwd(x, w1, w2, ts, seq_offsets, max_len: int, params: LayerParams, *, out=None,
-                   workspace=None, timing_events=None, products: int = HSTU_PRODUCTS_HIPBLASLT):
+                   workspace=None, timing_events=None, products: int = HSTU_PRODUCTS_AUTO):
     """Full layer: [U|V|Q|K] = SiLU(x w1), attention, out = A w2.
 
     x [T, E], w1 [E, 4*H*d], w2 [H*d, E], all bf16 on the GPU; ts int64 [T];
-    seq_offsets int32 [B+1]. products: HSTU_PRODUCTS_HIPBLASLT or
-    HSTU_PRODUCTS_OWN (the library's MFMA kernel). Returns out [T, E]."""
+    seq_offsets int32 [B+1]. products: HSTU_PRODUCTS_AUTO (default: f1 on the
+    library's MFMA kernel where it fits, f2 on hipBLASLt), HSTU_PRODUCTS_OWN
+    (both on the library's kernel) or HSTU_PRODUCTS_HIPBLASLT. Returns out [T, E]."""
     H, d = params.num_heads, params.head_dim
     for name, t in (("x", x), ("w1", w1), ("w2", w2)):
         _device_tensor(t, params.dtype, name)

@@ -186,13 +186,19 @@ hstu_status_t hstu_layer_fwd(const hstu_params_t* params, const hstu_layer_weigh
   if (params->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
   if (batch < 0 || total_tokens < 0 || max_len < 0 || weights->embed_dim < 1 || (weights->embed_dim % 8) != 0)
     return HSTU_ERR_INVALID_ARG;
-  if (weights->products != HSTU_PRODUCTS_HIPBLASLT && weights->products != HSTU_PRODUCTS_OWN)
+  const int32_t prod = weights->products;
+  if (prod != HSTU_PRODUCTS_HIPBLASLT && prod != HSTU_PRODUCTS_OWN && prod != HSTU_PRODUCTS_AUTO)
     return HSTU_ERR_INVALID_ARG;
-  const bool own = weights->products == HSTU_PRODUCTS_OWN;
-  if (own) {
+  bool own_fits;
+  {
     const int64_t hd = (int64_t)params->num_heads * params->head_dim, e = weights->embed_dim;
-    if ((4 * hd) % 256 != 0 || e % 256 != 0 || e % 64 != 0 || hd % 64 != 0) return HSTU_ERR_UNSUPPORTED;
+    own_fits = (4 * hd) % 256 == 0 && e % 256 == 0 && e % 64 == 0 && hd % 64 == 0;
   }
+  if (prod == HSTU_PRODUCTS_OWN && !own_fits) return HSTU_ERR_UNSUPPORTED;
+  // which product runs where: f1 on the own kernel for OWN, and for AUTO
+  // when it fits; f2 on the own kernel for OWN only
+  const bool own_f1 = prod == HSTU_PRODUCTS_OWN || (prod == HSTU_PRODUCTS_AUTO && own_fits);
+  const bool own_f2 = prod == HSTU_PRODUCTS_OWN;
   // the attention checks the remaining parameters; run them before anything is launched
   if (hstu_workspace_size(HSTU_FN_FULL, params, batch, total_tokens, max_len) == 0) return HSTU_ERR_INVALID_ARG;
   if (batch == 0 || total_tokens == 0) return HSTU_OK;
@@ -221,7 +227,7 @@ hstu_status_t hstu_layer_fwd(const hstu_params_t* params, const hstu_layer_weigh
   // f1 with SiLU into U, V, Q, K
   if (!mark(0)) return HSTU_ERR_LAUNCH;
   const char* w1 = (const char*)weights->w1;
-  if (own) {
+  if (own_f1) {
     // one product; the epilogue writes column block i to buffer i (the
     // buffers sit buf_elems apart in the workspace)
     hstu::GemmArgs g = {};
@@ -253,7 +259,7 @@ hstu_status_t hstu_layer_fwd(const hstu_params_t* params, const hstu_layer_weigh
   if (!mark(2)) return HSTU_ERR_LAUNCH;
 
   // f2: out = A W2
-  if (own) {
+  if (own_f2) {
     hstu::GemmArgs g = {};
     g.a = (const hstu::bf16*)a;
     g.b = (const hstu::bf16*)weights->w2;

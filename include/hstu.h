@@ -428,7 +428,11 @@ hstu_status_t hstu_pm_stats(hstu_page_manager_t* pm, int32_t* free_pages, int32_
  * the workspace) or HSTU_PRODUCTS_OWN (1, hstu_matmul_bf16: f1 as one
  * product with SiLU and the U/V/Q/K split fused in its epilogue; needs
  * 4*H*d and E multiples of 256 and E and H*d multiples of 64, else
- * HSTU_ERR_UNSUPPORTED). The attention runs on this library's kernels. Only HSTU_BF16 is supported (HSTU_ERR_UNSUPPORTED for
+ * HSTU_ERR_UNSUPPORTED) or HSTU_PRODUCTS_AUTO (2: f1 on hstu_matmul_bf16
+ * when those limits hold, else on hipBLASLt; f2 on hipBLASLt. On the
+ * 16-user E = 1,024 layer the own kernel is the faster f1, whose SiLU and
+ * split it fuses, and hipBLASLt the faster f2). The attention runs on this
+ * library's kernels. Only HSTU_BF16 is supported (HSTU_ERR_UNSUPPORTED for
  * HSTU_F32): bf16 operands, fp32 accumulation, bf16 U, V, Q, K, A and out.
  *   weights->w1, weights->w2  row-major device matrices in bf16
  *   x    [T, E] bf16; ts int64 [T]; out [T, E] bf16 (must not alias x)
@@ -439,7 +443,7 @@ hstu_status_t hstu_pm_stats(hstu_page_manager_t* pm, int32_t* free_pages, int32_
  * host state the library holds); later calls reuse it and the chosen GEMM
  * algorithms. Callable from several host threads.
  */
-typedef enum { HSTU_PRODUCTS_HIPBLASLT = 0, HSTU_PRODUCTS_OWN = 1 } hstu_products_t;
+typedef enum { HSTU_PRODUCTS_HIPBLASLT = 0, HSTU_PRODUCTS_OWN = 1, HSTU_PRODUCTS_AUTO = 2 } hstu_products_t;
 
 typedef struct {
   int32_t embed_dim;  /* E >= 1, multiple of 8 */

@@ -238,8 +238,11 @@ def test_layer_workspace_and_bad_arguments_before_launch():
     assert call(_params(dtype=0)) == UNSUPPORTED
     assert call(p, w=hs._LayerWeights(1020, FAKE, FAKE)) == INVALID
     assert call(p, w=hs._LayerWeights(1024, None, FAKE)) == INVALID
-    assert call(p, w=hs._LayerWeights(1024, FAKE, FAKE, 2)) == INVALID       # unknown product backend
+    assert call(p, w=hs._LayerWeights(1024, FAKE, FAKE, 3)) == INVALID       # unknown product backend
     assert call(p, w=hs._LayerWeights(1000, FAKE, FAKE, 1)) == UNSUPPORTED   # own products need E % 256 == 0
+    # AUTO falls back to hipBLASLt where the own kernel does not fit: the
+    # call gets as far as the workspace check
+    assert call(p, w=hs._LayerWeights(1000, FAKE, FAKE, 2)) == WORKSPACE
     assert call(p, x=None) == INVALID
     assert call(p, x=FAKE + 2) == INVALID
     assert call(_params(head_dim=48)) == INVALID

@@ -13,7 +13,7 @@ from devutil import TOL, dev, to_np
 pytestmark = pytest.mark.gpu
 
 
-PRODUCTS = [hs.HSTU_PRODUCTS_HIPBLASLT, hs.HSTU_PRODUCTS_OWN]
+PRODUCTS = [hs.HSTU_PRODUCTS_HIPBLASLT, hs.HSTU_PRODUCTS_OWN, hs.HSTU_PRODUCTS_AUTO]
 
 
 def run_layer(inp, **kw):
