@@ -201,13 +201,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if ((int64_t)blockIdx.x >= (int64_t)ldc(a.count)) return;
-  const WorkItem it = ldc(a.items + blockIdx.x);
+  const int32_t count = ldc(a.count);
+  const WorkItem it = ldc(a.items + blockIdx.x);  // in bounds for every workgroup of the grid
+  if ((int64_t)blockIdx.x >= (int64_t)count) return;
   const int b = it.b, h = it.h, q_start = it.q_start, q_len = it.q_len;
   const int k_begin = it.k_begin, k_end = it.k_end;
   const int H = a.H;
-  const int64_t q_off = ldc(a.offsets + b);
-  const int L = ldc(a.offsets + b + 1) - (int)q_off;
+  const int64_t q_off = it.off;
+  const int L = it.L;
   const int n_norm = a.norm_n > 0 ? a.norm_n : L;
   const int n_pos = a.pos_tab ? a.n_pos : 1;
   load_bwd_tables(a, h, tab, n_pos);
@@ -460,12 +461,13 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
   const int tid = threadIdx.x;
   const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if ((int64_t)blockIdx.x >= (int64_t)ldc(a.count)) return;
-  const WorkItem it = ldc(a.items + blockIdx.x);
+  const int32_t count = ldc(a.count);
+  const WorkItem it = ldc(a.items + blockIdx.x);  // in bounds for every workgroup of the grid
+  if ((int64_t)blockIdx.x >= (int64_t)count) return;
   const int b = it.b, h = it.h;
   const int H = a.H;
-  const int64_t q_off = ldc(a.offsets + b);
-  const int L = ldc(a.offsets + b + 1) - (int)q_off;
+  const int64_t q_off = it.off;
+  const int L = it.L;
   const int n_norm = a.norm_n > 0 ? a.norm_n : L;
   const int nq = (int)ceil_div(L, QT);
   const int k0 = (nq - 1 - it.q_start / QT) * QT;  // mirrored key block

@@ -55,31 +55,34 @@ void attn_fwd_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave facts in SGPRs
-  if ((int64_t)blockIdx.x >= (int64_t)ldc(a.count)) return;
+  // the item and the count load together (the item array holds an entry for
+  // every workgroup of the grid; one past the count is never used)
+  const int32_t count = ldc(a.count);
   const WorkItem it = ldc(a.items + blockIdx.x);
+  if ((int64_t)blockIdx.x >= (int64_t)count) return;
   const int b = it.b, h = it.h, kind = it.kind;
   const int q_start = it.q_start, q_len = it.q_len;
   const int k_begin = it.k_begin, k_end = it.k_end;
   const int H = a.H;
 
   // ---- per-user geometry -------------------------------------------------
-  const int64_t q_off = ldc(a.offsets + b);
-  const int Lq = ldc(a.offsets + b + 1) - (int)q_off;
+  const int64_t q_off = it.off;
+  const int Lq = it.L;
   int kcount, pos0, n_norm;
   bool cand = false;
   if (MODE == MODE_CACHED) {
-    const int C = ldc(a.cache_lens + b);
+    const int C = it.X;
     kcount = C + Lq;
     pos0 = C + q_start;
     n_norm = C + Lq;
   } else if (MODE == MODE_MFALCON_PAGED) {
-    const int C = ldc(a.cache_lens + b);  // history length; every row is a candidate at position C
+    const int C = it.X;  // history length; every row is a candidate at position C
     kcount = C;
     cand = true;
     pos0 = C;
     n_norm = C + 1;
   } else if (MODE == MODE_MFALCON) {
-    const int n = Lq - ldc(a.num_cand + b);
+    const int n = Lq - it.X;
     kcount = n;
     cand = (kind == KIND_CANDIDATE);
     pos0 = cand ? n : q_start;

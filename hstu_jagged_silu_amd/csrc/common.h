@@ -37,9 +37,16 @@ constexpr int PAGE = 64;           // page size of the paged KV cache (one key t
 // One unit of attention work: query rows [q_start, q_start + q_len) of user
 // b (local indices), head h, against keys [k_begin, k_end). `chunk` numbers
 // the key split of the KV-cache path (0 elsewhere).
+// One work item of the attention kernels. The user's first row, row count
+// and per-mode count (cached prefix or candidates) ride along, so that a
+// workgroup needs no dependent load of the per-user arrays before it starts.
 struct WorkItem {
   int32_t b, h, chunk, kind;
   int32_t q_start, q_len, k_begin, k_end;
+  int32_t off;   // offsets[b]
+  int32_t L;     // offsets[b + 1] - offsets[b]
+  int32_t X;     // cache_lens[b] (paged modes), num_cand[b] (M-FALCON), else 0
+  int32_t pad;
 };
 
 // Workspace layout (bytes), shared by the scheduler, the attention kernel

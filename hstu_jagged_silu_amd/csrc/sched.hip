@@ -34,12 +34,13 @@ struct UserGeo {
 // What the work list needs to know of one user: its query rows, and its
 // cached prefix (paged modes) or candidate count (M-FALCON).
 struct UserRaw {
-  int L, X;
+  int L, X, off;
 };
 
 __device__ inline UserRaw user_raw(const SchedArgs& a, int b) {
   UserRaw r;
-  r.L = max(0, a.offsets[b + 1] - a.offsets[b]);
+  r.off = a.offsets[b];
+  r.L = max(0, a.offsets[b + 1] - r.off);
   r.X = mode_paged(a.mode) ? a.cache_lens[b] : (a.mode == MODE_MFALCON ? a.num_cand[b] : 0);
   return r;
 }
@@ -91,6 +92,10 @@ __device__ inline WorkItem make_item(const SchedArgs& a, int b, UserRaw r, int l
   const int per_head = user_items_per_head(a, g);
   WorkItem w;
   w.b = b;
+  w.off = r.off;
+  w.L = r.L;
+  w.X = r.X;
+  w.pad = 0;
   w.h = local / per_head;
   int t = local % per_head;
   w.chunk = 0;
