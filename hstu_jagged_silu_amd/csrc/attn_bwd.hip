@@ -67,10 +67,11 @@ struct RabHist {
   float time[NWAVES][64];           // per time bucket
 };
 
+template <int NT = NTHREADS>
 __device__ inline void load_bwd_tables(const BwdArgs& a, int h, BwdTables& tab, int n_pos) {
   const int tid = threadIdx.x;
   const float* pt = a.pos_tab ? a.pos_tab + (int64_t)h * a.pos_stride : nullptr;
-  for (int i = tid; i < n_pos; i += NTHREADS) tab.pos_t[i] = pt ? pt[i] * -LOG2E : 0.0f;
+  for (int i = tid; i < n_pos; i += NT) tab.pos_t[i] = pt ? pt[i] * -LOG2E : 0.0f;
   if (tid < 64) {
     float t = 0.0f;
     if (a.time_tab) t = a.time_tab[(int64_t)h * a.time_stride + min(63 - tid, a.n_time - 1)] * -LOG2E;
@@ -119,11 +120,14 @@ __device__ inline void silu_fwd_bwd(float y, float dp, float& p, float& ds) {
 }
 
 // Stage HBM -> LDS of KT rows of two [T, H, D] tensors (rows r0 .. r0 + KT - 1
-// of head h, clamped to the last valid row) plus their timestamps.
-template <int D>
+// of head h, clamped to the last valid row) plus their timestamps, by the NW
+// waves of the workgroup.
+template <int D, int NW = NWAVES>
 __device__ inline void stage_rows(const BwdArgs& a, const void* x0, const void* x1, Stage<bf16, D>& st, int64_t r0,
                                   int nvalid, int h, int64_t& tsreg) {
   using G = Geo<bf16, D>;
+  constexpr int ND = G::TILE / (NW * 1024);  // 1 KB LDS DMA instructions per wave and tensor
+  static_assert(ND >= 1 && ND * NW * 1024 == G::TILE, "tile staging map");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int last = max(nvalid - 1, 0);
@@ -131,8 +135,8 @@ __device__ inline void stage_rows(const BwdArgs& a, const void* x0, const void* 
   const unsigned char* b0 = (const unsigned char*)x0 + ((r0 * a.H + h) * D) * 2;
   const unsigned char* b1 = (const unsigned char*)x1 + ((r0 * a.H + h) * D) * 2;
   #pragma unroll
-  for (int i = 0; i < G::NDMA; ++i) {
-    const int base = (wave * G::NDMA + i) * 64;
+  for (int i = 0; i < ND; ++i) {
+    const int base = (wave * ND + i) * 64;
     const int P = base + lane;
     const int r = P / G::CPR, pc = P % G::CPR;
     const int64_t off = min(r, last) * rstride + ((pc ^ swz_b<D>(r)) << 4);
@@ -672,6 +676,321 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
 }
 
 // ============================================================================
+// dK and dV for d = 128: eight waves, two per SIMD
+// ============================================================================
+// The four-wave kernel above keeps K, V and both accumulators of its 32 keys
+// in registers (344 and more), so it runs one wave per SIMD, and a lone wave
+// in order of issue leaves the matrix unit idle while it waits on LDS reads
+// and computes the SiLU. Here K and V of the workgroup's 128 keys stay in LDS
+// for the whole item, which brings a wave under 256 registers: wave w owns the
+// 32 keys of group w mod 4 and the query half w / 4 of every 64-query tile,
+// and the two waves of a SIMD cover each other's waits. The two query halves
+// keep partial dK and dV sums that are added through LDS at the end, half 0
+// first, so the result does not depend on wave timing.
+constexpr int DKDV8_WAVES = 8;
+constexpr int DKDV8_THREADS = 64 * DKDV8_WAVES;
+
+struct Dkdv8Smem {
+  unsigned char kres[QT * 256] __attribute__((aligned(16)));  // K rows of the key block, swz_b<128> layout
+  unsigned char vres[QT * 256] __attribute__((aligned(16)));  // V rows
+  Stage<bf16, 128> st[2];                                     // Q (k) and dO (v) tiles of 64 queries
+};
+// the end of the kernel reuses the whole of it: partial sums of half 1, then
+// the fp32 rows of dV and dK on their way out (2 x 128 x 128 x 4 bytes each)
+static_assert(sizeof(Dkdv8Smem) >= 2 * QT * 128 * 4, "reduction buffer");
+
+__global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArgs a) {
+  constexpr int D = 128;
+  using T = bf16;
+  using G = Geo<T, D>;
+  using M = Mfma<T>;
+  static_assert(G::ROWB == 256 && G::CPR == 16, "resident key rows of 256 bytes");
+  __shared__ Dkdv8Smem sm;
+  __shared__ BwdTables tab;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave & 3, qb = wave >> 2;  // key group, query half
+  const int32_t count = ldc(a.count);
+  const WorkItem it = ldc(a.items + blockIdx.x);  // in bounds for every workgroup of the grid
+  if ((int64_t)blockIdx.x >= (int64_t)count) return;
+  const int h = it.h;
+  const int H = a.H;
+  const int64_t q_off = it.off;
+  const int L = it.L;
+  const int n_norm = a.norm_n > 0 ? a.norm_n : L;
+  const int nq = (int)ceil_div(L, QT);
+  const int k0 = (nq - 1 - it.q_start / QT) * QT;  // mirrored key block
+  const int klen = min(QT, L - k0);
+  const int n_pos = a.pos_tab ? a.n_pos : 1;
+  load_bwd_tables<DKDV8_THREADS>(a, h, tab, n_pos);
+
+  // K and V of the 128 keys into LDS (rows past the user's end are copies of
+  // its last row; their pairs are masked): 2,048 16-byte chunks per tensor
+  {
+    const int64_t rstride = (int64_t)H * G::ROWB;
+    const unsigned char* kb = (const unsigned char*)a.k + (((q_off + k0) * H + h) * D) * 2;
+    const unsigned char* vb = (const unsigned char*)a.v + (((q_off + k0) * H + h) * D) * 2;
+    constexpr int NR = QT * G::CPR / DKDV8_THREADS;  // chunks per lane and tensor
+    #pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int base = (wave * NR + i) * 64;
+      const int P = base + lane;
+      const int r = P / G::CPR, pc = P % G::CPR;
+      const int64_t off = min(r, klen - 1) * rstride + ((pc ^ swz_b<D>(r)) << 4);
+      __builtin_amdgcn_global_load_lds((const void*)(kb + off), LDS_PTR(void, sm.kres + base * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vb + off), LDS_PTR(void, sm.vres + base * 16), 16, 0, 0);
+    }
+  }
+
+  const int key_w = kg * 32 + l32;
+  const bool key_ok = key_w < klen;
+  const int kc = min(key_w, klen - 1);
+  const int64_t krow = q_off + k0 + kc;
+  const int kpos = k0 + kc;
+  const int64_t tsk = a.ts[krow];
+  const int w_first = kg * 32;
+  const bool w_keys = w_first < klen;
+  const bool w_full = w_first + 31 < klen;          // every key of the wave valid
+  const int w_kmin = k0 + w_first, w_kmax = k0 + min(w_first + 31, klen - 1);
+  int64_t w_ts_min = key_ok ? tsk : INT64_MAX, w_ts_max = key_ok ? tsk : INT64_MIN;
+  for (int m = 32; m >= 1; m >>= 1) {
+    w_ts_min = min(w_ts_min, shfl_xor64(w_ts_min, m));
+    w_ts_max = max(w_ts_max, shfl_xor64(w_ts_max, m));
+  }
+  w_ts_min = uniform64(w_ts_min);
+  w_ts_max = uniform64(w_ts_max);
+  const int n_time_eff = a.time_tab ? min(a.n_time, 64) : 1;
+
+  // operand offsets: Q / dO rows of this half (A operand, rows in the order
+  // of M::krow so the accumulators are the B operands of dV and dK), K / V
+  // rows of this key group (B operand), and the transposing reads
+  const int qr = M::krow(0, l32) + 32 * qb;
+  const uint32_t qbase = (uint32_t)(qr * G::ROWB), kbase = (uint32_t)(key_w * G::ROWB);
+  const int qsw = swz_b<D>(qr), ksw = swz_b<D>(key_w);
+  uint32_t qtr[G::NDB][2];
+  #pragma unroll
+  for (int db = 0; db < G::NDB; ++db) {
+    qtr[db][0] = tr_off_b<D>(lane, db, 0, 0);
+    qtr[db][1] = tr_off_b<D>(lane, db, 0, 1);
+  }
+  f32x16 dkacc[G::NDB], dvacc[G::NDB];
+  #pragma unroll
+  for (int i = 0; i < G::NDB; ++i) { dkacc[i] = f32x16{}; dvacc[i] = f32x16{}; }
+  const float sc = a.alpha * -LOG2E;
+  const bool has_time = a.time_tab != nullptr;
+  using LB = __attribute__((address_space(3))) unsigned char;
+  using LV = __attribute__((address_space(3))) const bf16x8;
+  using LT = __attribute__((address_space(3))) v4i16;
+  LB* kl = LDS_PTR(unsigned char, sm.kres);
+  LB* vl = LDS_PTR(unsigned char, sm.vres);
+
+  auto compute_tile = [&](Stage<T, D>& st, int j0) {
+    // every query of this half precedes every key of this wave: all masked
+    if (!w_keys || j0 + 32 * qb + 31 < w_kmin) return;
+    // one bias constant and no mask for the whole wave tile? (as in the forward)
+    const bool need_mask = !w_full || j0 < w_kmax || j0 + KT > L;
+    const bool pos_uniform = (a.pos_tab == nullptr) || (j0 - w_kmax >= n_pos - 1);
+    bool time_uniform = !has_time;
+    int z_tile = 63;
+    bool small_span = true;
+    if (has_time) {
+      const int64_t r0 = q_off + j0;
+      const int64_t i0 = min(r0 / KT, a.n_stat_blocks - 1), i1 = min((r0 + KT - 1) / KT, a.n_stat_blocks - 1);
+      int64_t q_min = min(ldc(a.tstats + 2 * i0), ldc(a.tstats + 2 * i1));
+      int64_t q_max = max(ldc(a.tstats + 2 * i0 + 1), ldc(a.tstats + 2 * i1 + 1));
+      if (q_min > q_max) q_min = q_max = w_ts_min;
+      // rows past the user's end (last tile) are clamped copies of its last row
+      const int64_t d1 = q_max - w_ts_min, d2 = w_ts_max - q_min;
+      small_span = max(d1 < 0 ? -d1 : d1, d2 < 0 ? -d2 : d2) < ((int64_t)1 << 31) - 2;
+      int64_t lo = -1, hi = -1;
+      if (q_min >= w_ts_max) { lo = q_min - w_ts_max; hi = q_max - w_ts_min; }
+      else if (w_ts_min >= q_max) { lo = w_ts_min - q_max; hi = w_ts_max - q_min; }
+      if (lo >= 0 && !need_mask && pos_uniform) {
+        const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
+        if (min(63 - zlo, n_time_eff - 1) == min(63 - zhi, n_time_eff - 1)) { time_uniform = true; z_tile = zlo; }
+      }
+    }
+    const bool fast = pos_uniform && time_uniform && !need_mask;
+    const float c_uni = (a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f) + (has_time ? tab.time_t[z_tile] : 0.0f);
+    const int64_t* ts_l = st.ts64 + M::HLK * hl;
+    const int32_t* tsl_lo = st.ts_lo + M::HLK * hl;
+    const int32_t tsk_lo = (int32_t)tsk;
+    LB* ql = LDS_PTR(unsigned char, st.k);
+    LB* gl = LDS_PTR(unsigned char, st.v);
+    // S = Q K^T and dP = dO V^T over the 32 queries of this half; the
+    // operands of step i + 1 are read while the MFMAs of step i run (one step
+    // ahead only: reading further ahead costs registers the two waves of a
+    // SIMD do not have)
+    f32x16 s = f32x16{}, dp = f32x16{};
+    bf16x8 op[2][4];
+    auto read_step = [&](int i, bf16x8* o) {
+      const uint32_t qo = qbase + (((2 * i + hl) ^ qsw) << 4), ko = kbase + (((2 * i + hl) ^ ksw) << 4);
+      o[0] = *(LV*)(ql + qo);
+      o[1] = *(LV*)(kl + ko);
+      o[2] = *(LV*)(gl + qo);
+      o[3] = *(LV*)(vl + ko);
+    };
+    read_step(0, op[0]);
+    #pragma unroll
+    for (int i = 0; i < G::NQOP; ++i) {
+      if (i + 1 < G::NQOP) read_step(i + 1, op[(i + 1) & 1]);
+      s = M::run(op[i & 1][0], op[i & 1][1], s);
+      dp = M::run(op[i & 1][2], op[i & 1][3], dp);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bf16x8 pb[2], dsb[2];
+    if (fast) {
+      #pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float p, ds;
+        silu_fwd_bwd(fmaf(s[v], sc, c_uni), dp[v], p, ds);
+        pb[v >> 3][v & 7] = (bf16)p;
+        dsb[v >> 3][v & 7] = (bf16)ds;
+      }
+    } else {
+      auto general = [&](auto small_tag) {
+        constexpr bool SMALL = decltype(small_tag)::value;
+        float cb[16];
+        if (a.pos_tab) {
+          #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rel = j0 + M::key_of(qb, v, hl) - kpos;
+            cb[v] = tab.pos_t[min((unsigned)rel, (unsigned)(n_pos - 1))];
+          }
+        } else {
+          #pragma unroll
+          for (int v = 0; v < 16; ++v) cb[v] = 0.0f;
+        }
+        if (has_time) {
+          #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int qv = M::key_of(qb, v, 0);
+            cb[v] += tab.time_t[time_z<SMALL>(SMALL ? 0 : ts_l[qv], tsk, SMALL ? tsl_lo[qv] : 0, tsk_lo)];
+          }
+        }
+        #pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int qpos = j0 + M::key_of(qb, v, hl);  // query row
+          const bool ok = key_ok && qpos >= kpos && qpos < L;
+          float p, ds;
+          silu_fwd_bwd(ok ? fmaf(s[v], sc, cb[v]) : MASKED_Y, dp[v], p, ds);
+          pb[v >> 3][v & 7] = (bf16)p;
+          dsb[v >> 3][v & 7] = (bf16)ds;
+        }
+      };
+      if (small_span) general(std::true_type{});
+      else general(std::false_type{});
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries of this half,
+    // the transposed operands of step db + 1 read during the MFMAs of step db
+    bf16x8 tp[2][4];
+    auto read_tr = [&](int db, bf16x8* o) {
+      #pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int off = (2 * qb + cc) * 16 * G::ROWB;
+        const v4i16 glo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(gl + qtr[db][0] + off));
+        const v4i16 ghi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(gl + qtr[db][1] + off));
+        const v4i16 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(ql + qtr[db][0] + off));
+        const v4i16 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(ql + qtr[db][1] + off));
+        o[cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[2 + cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    read_tr(0, tp[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+      if (db + 1 < G::NDB) read_tr(db + 1, tp[(db + 1) & 1]);
+      #pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        dvacc[db] = M::run(tp[db & 1][cc], pb[cc], dvacc[db]);
+        dkacc[db] = M::run(tp[db & 1][2 + cc], dsb[cc], dkacc[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  const int ntiles = (int)ceil_div(L - k0, KT);
+  int64_t tsreg = 0;
+  auto issue = [&](Stage<T, D>& st, int j0) {
+    stage_rows<D, DKDV8_WAVES>(a, a.q, a.dout, st, q_off + j0, min(KT, L - j0), h, tsreg);
+  };
+  // one call site for the tile body (the stage is picked at run time), so the
+  // compiler keeps one set of operand addresses; a stage is refilled only
+  // after the barrier that ends every wave's reads of it
+  issue(sm.st[0], k0);
+  finish_stage<D>(sm.st[0], tsreg);  // also waits for the K and V rows
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = k0 + t * KT, cur = t & 1;
+    if (t + 1 < ntiles) issue(sm.st[cur ^ 1], j0 + KT);
+    compute_tile(sm.st[cur], j0);
+    if (t + 1 < ntiles) finish_stage<D>(sm.st[cur ^ 1], tsreg);
+  }
+
+  // half 1 hands its partial sums to half 0: [tensor][key group][db][4][lane] x f32x4
+  __syncthreads();
+  __attribute__((address_space(3))) f32x4* red = LDS_PTR(f32x4, &sm);
+  auto ridx = [&](int t, int db, int g) { return (((t * 4 + kg) * G::NDB + db) * 4 + g) * 64 + lane; };
+  if (qb == 1) {
+    #pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+      #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        red[ridx(0, db, g)] = f32x4{dvacc[db][4 * g], dvacc[db][4 * g + 1], dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]};
+        red[ridx(1, db, g)] = f32x4{dkacc[db][4 * g], dkacc[db][4 * g + 1], dkacc[db][4 * g + 2], dkacc[db][4 * g + 3]};
+      }
+    }
+  }
+  __syncthreads();
+  if (qb == 0) {
+    #pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+      #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = red[ridx(0, db, g)], y = red[ridx(1, db, g)];
+        #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dvacc[db][4 * g + j] += x[j];
+          dkacc[db][4 * g + j] += y[j];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // fp32 rows of dV and dK in LDS ([tensor][128 rows][D], 16-byte chunk c of
+  // row r at c xor (r mod 32)), then bf16 rows out by all eight waves
+  constexpr int OCPR = D / 4;
+  __attribute__((address_space(3))) float* ost = LDS_PTR(float, &sm);
+  if (qb == 0) {
+    const float sv = -LN2 / (float)n_norm, sk = a.alpha / (float)n_norm;
+    const int row_w = key_w;
+    #pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+      #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = (32 * db + 8 * g + 4 * hl) / 4;
+        const int off = row_w * D + (c ^ (row_w % OCPR)) * 4;
+        *(__attribute__((address_space(3))) f32x4*)(ost + off) =
+            f32x4{dvacc[db][4 * g] * sv, dvacc[db][4 * g + 1] * sv, dvacc[db][4 * g + 2] * sv, dvacc[db][4 * g + 3] * sv};
+        *(__attribute__((address_space(3))) f32x4*)(ost + QT * D + off) =
+            f32x4{dkacc[db][4 * g] * sk, dkacc[db][4 * g + 1] * sk, dkacc[db][4 * g + 2] * sk, dkacc[db][4 * g + 3] * sk};
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < 2 * QT * OCPR; i += DKDV8_THREADS) {
+    const int t = i / (QT * OCPR), r = (i / OCPR) % QT, c = i % OCPR;
+    if (r < klen) {
+      const f32x4 x = *(__attribute__((address_space(3))) const f32x4*)(ost + t * QT * D + r * D + (c ^ (r % OCPR)) * 4);
+      const bf16x4 v = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+      *(bf16x4*)((bf16*)(t == 0 ? a.dv : a.dk) + ((q_off + k0 + r) * H + h) * D + c * 4) = v;
+    }
+  }
+}
+
+// ============================================================================
 // Bias-table gradients: add the per-item histograms in canonical order
 // ============================================================================
 // Block (x, y): 64 buckets of table row y (a head, or the one shared row;
@@ -721,7 +1040,7 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int D, int64_t grid, hipStream_t s)
   const dim3 g((unsigned)grid), blk(NTHREADS);
   if (D == 128) {
     hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, g, blk, 0, s, a);
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, g, blk, 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv8_kernel, g, dim3(DKDV8_THREADS), 0, s, a);
   } else if (D == 64) {
     hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, g, blk, 0, s, a);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, g, blk, 0, s, a);
