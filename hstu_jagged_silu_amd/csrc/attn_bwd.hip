@@ -690,14 +690,19 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
 constexpr int DKDV8_WAVES = 8;
 constexpr int DKDV8_THREADS = 64 * DKDV8_WAVES;
 
-struct Dkdv8Smem {
-  unsigned char kres[QT * 256] __attribute__((aligned(16)));  // K rows of the key block, swz_b<128> layout
-  unsigned char vres[QT * 256] __attribute__((aligned(16)));  // V rows
-  Stage<bf16, 128> st[2];                                     // Q (k) and dO (v) tiles of 64 queries
+// K and V rows of the key block (swz_b<128> layout). The two Q/dO stages are
+// LDS objects of their own, as in the forward, so the compiler sees that the
+// DMA into one stage cannot touch the reads of the other and does not wait
+// for it.
+struct Dkdv8Keys {
+  unsigned char k[QT * 256] __attribute__((aligned(16)));
+  unsigned char v[QT * 256] __attribute__((aligned(16)));
 };
-// the end of the kernel reuses the whole of it: partial sums of half 1, then
-// the fp32 rows of dV and dK on their way out (2 x 128 x 128 x 4 bytes each)
-static_assert(sizeof(Dkdv8Smem) >= 2 * QT * 128 * 4, "reduction buffer");
+// The end of the kernel reuses all three: the fp32 partial sums of half 1,
+// then the fp32 rows of dV and dK on their way out; dV's 64 KB go to the key
+// rows, dK's to the two stages (32 KB each).
+static_assert(sizeof(Dkdv8Keys) == QT * 128 * 4 && sizeof(Stage<bf16, 128>) >= QT / 2 * 128 * 4,
+              "reduction buffers");
 
 __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArgs a) {
   constexpr int D = 128;
@@ -705,7 +710,9 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
   using G = Geo<T, D>;
   using M = Mfma<T>;
   static_assert(G::ROWB == 256 && G::CPR == 16, "resident key rows of 256 bytes");
-  __shared__ Dkdv8Smem sm;
+  __shared__ Stage<T, D> st0;
+  __shared__ Stage<T, D> st1;
+  __shared__ Dkdv8Keys kv;
   __shared__ BwdTables tab;
 
   const int tid = threadIdx.x;
@@ -739,8 +746,8 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
       const int P = base + lane;
       const int r = P / G::CPR, pc = P % G::CPR;
       const int64_t off = min(r, klen - 1) * rstride + ((pc ^ swz_b<D>(r)) << 4);
-      __builtin_amdgcn_global_load_lds((const void*)(kb + off), LDS_PTR(void, sm.kres + base * 16), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vb + off), LDS_PTR(void, sm.vres + base * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(kb + off), LDS_PTR(void, kv.k + base * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vb + off), LDS_PTR(void, kv.v + base * 16), 16, 0, 0);
     }
   }
 
@@ -763,18 +770,16 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
   w_ts_max = uniform64(w_ts_max);
   const int n_time_eff = a.time_tab ? min(a.n_time, 64) : 1;
 
-  // operand offsets: Q / dO rows of this half (A operand, rows in the order
-  // of M::krow so the accumulators are the B operands of dV and dK), K / V
-  // rows of this key group (B operand), and the transposing reads
+  // Operand offsets. Q / dO rows of this half (A operand, rows in the order
+  // of M::krow so the accumulators are the B operands of dV and dK) and K / V
+  // rows of this key group (B operand): the chunk of step i of row r sits at
+  // r * 256 + ((2i + hl) xor swz(r)) * 16 = (r * 256 + (hl xor swz(r)) * 16)
+  // xor 32i. Transposing reads of d block db: the offset of block 0 xor 64db.
   const int qr = M::krow(0, l32) + 32 * qb;
-  const uint32_t qbase = (uint32_t)(qr * G::ROWB), kbase = (uint32_t)(key_w * G::ROWB);
-  const int qsw = swz_b<D>(qr), ksw = swz_b<D>(key_w);
-  uint32_t qtr[G::NDB][2];
-  #pragma unroll
-  for (int db = 0; db < G::NDB; ++db) {
-    qtr[db][0] = tr_off_b<D>(lane, db, 0, 0);
-    qtr[db][1] = tr_off_b<D>(lane, db, 0, 1);
-  }
+  const uint32_t q_base = (uint32_t)(qr * G::ROWB + ((hl ^ swz_b<D>(qr)) << 4));
+  const uint32_t k_base = (uint32_t)(key_w * G::ROWB + ((hl ^ swz_b<D>(key_w)) << 4));
+  const uint32_t t_base0 = tr_off_b<D>(lane, 0, 0, 0) + qb * 32 * G::ROWB;
+  const uint32_t t_base1 = tr_off_b<D>(lane, 0, 0, 1) + qb * 32 * G::ROWB;
   f32x16 dkacc[G::NDB], dvacc[G::NDB];
   #pragma unroll
   for (int i = 0; i < G::NDB; ++i) { dkacc[i] = f32x16{}; dvacc[i] = f32x16{}; }
@@ -783,8 +788,8 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
   using LB = __attribute__((address_space(3))) unsigned char;
   using LV = __attribute__((address_space(3))) const bf16x8;
   using LT = __attribute__((address_space(3))) v4i16;
-  LB* kl = LDS_PTR(unsigned char, sm.kres);
-  LB* vl = LDS_PTR(unsigned char, sm.vres);
+  LB* kl = LDS_PTR(unsigned char, kv.k);
+  LB* vl = LDS_PTR(unsigned char, kv.v);
 
   auto compute_tile = [&](Stage<T, D>& st, int j0) {
     // every query of this half precedes every key of this wave: all masked
@@ -823,10 +828,14 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
     // operands of step i + 1 are read while the MFMAs of step i run (one step
     // ahead only: reading further ahead costs registers the two waves of a
     // SIMD do not have)
+    // the bases pass through an empty asm so that the offsets derived from
+    // them are formed here, in every tile, instead of being kept in registers
+    uint32_t qb_t = q_base, kb_t = k_base, tb0 = t_base0, tb1 = t_base1;
+    asm volatile("" : "+v"(qb_t), "+v"(kb_t), "+v"(tb0), "+v"(tb1));
     f32x16 s = f32x16{}, dp = f32x16{};
     bf16x8 op[2][4];
     auto read_step = [&](int i, bf16x8* o) {
-      const uint32_t qo = qbase + (((2 * i + hl) ^ qsw) << 4), ko = kbase + (((2 * i + hl) ^ ksw) << 4);
+      const uint32_t qo = qb_t ^ (uint32_t)(i << 5), ko = kb_t ^ (uint32_t)(i << 5);
       o[0] = *(LV*)(ql + qo);
       o[1] = *(LV*)(kl + ko);
       o[2] = *(LV*)(gl + qo);
@@ -889,11 +898,12 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
     auto read_tr = [&](int db, bf16x8* o) {
       #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        const int off = (2 * qb + cc) * 16 * G::ROWB;
-        const v4i16 glo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(gl + qtr[db][0] + off));
-        const v4i16 ghi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(gl + qtr[db][1] + off));
-        const v4i16 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(ql + qtr[db][0] + off));
-        const v4i16 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(ql + qtr[db][1] + off));
+        const uint32_t o0 = (tb0 ^ (uint32_t)(db << 6)) + cc * 16 * G::ROWB;
+        const uint32_t o1 = (tb1 ^ (uint32_t)(db << 6)) + cc * 16 * G::ROWB;
+        const v4i16 glo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(gl + o0));
+        const v4i16 ghi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(gl + o1));
+        const v4i16 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(ql + o0));
+        const v4i16 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(ql + o1));
         o[cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[2 + cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
@@ -917,29 +927,33 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
   auto issue = [&](Stage<T, D>& st, int j0) {
     stage_rows<D, DKDV8_WAVES>(a, a.q, a.dout, st, q_off + j0, min(KT, L - j0), h, tsreg);
   };
-  // one call site for the tile body (the stage is picked at run time), so the
-  // compiler keeps one set of operand addresses; a stage is refilled only
-  // after the barrier that ends every wave's reads of it
-  issue(sm.st[0], k0);
-  finish_stage<D>(sm.st[0], tsreg);  // also waits for the K and V rows
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = k0 + t * KT, cur = t & 1;
-    if (t + 1 < ntiles) issue(sm.st[cur ^ 1], j0 + KT);
-    compute_tile(sm.st[cur], j0);
-    if (t + 1 < ntiles) finish_stage<D>(sm.st[cur ^ 1], tsreg);
+  issue(st0, k0);
+  finish_stage<D>(st0, tsreg);  // also waits for the K and V rows
+  for (int t = 0; t < ntiles; t += 2) {
+    const int j0 = k0 + t * KT;
+    if (t + 1 < ntiles) issue(st1, j0 + KT);
+    compute_tile(st0, j0);
+    if (t + 1 >= ntiles) break;
+    finish_stage<D>(st1, tsreg);
+    if (t + 2 < ntiles) issue(st0, j0 + 2 * KT);
+    compute_tile(st1, j0 + KT);
+    if (t + 2 < ntiles) finish_stage<D>(st0, tsreg);
   }
 
-  // half 1 hands its partial sums to half 0: [tensor][key group][db][4][lane] x f32x4
+  // half 1 hands its partial sums to half 0, per tensor [key group][db][4][lane]
+  // x f32x4: dV's in the key rows, dK's in stage 0 (key groups 0, 1) and
+  // stage 1 (key groups 2, 3)
   __syncthreads();
-  __attribute__((address_space(3))) f32x4* red = LDS_PTR(f32x4, &sm);
-  auto ridx = [&](int t, int db, int g) { return (((t * 4 + kg) * G::NDB + db) * 4 + g) * 64 + lane; };
+  using LF4 = __attribute__((address_space(3))) f32x4;
+  LF4* red_v = LDS_PTR(f32x4, &kv) + kg * (G::NDB * 4 * 64) + lane;
+  LF4* red_k = LDS_PTR(f32x4, kg < 2 ? (void*)&st0 : (void*)&st1) + (kg & 1) * (G::NDB * 4 * 64) + lane;
   if (qb == 1) {
     #pragma unroll
     for (int db = 0; db < G::NDB; ++db) {
       #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        red[ridx(0, db, g)] = f32x4{dvacc[db][4 * g], dvacc[db][4 * g + 1], dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]};
-        red[ridx(1, db, g)] = f32x4{dkacc[db][4 * g], dkacc[db][4 * g + 1], dkacc[db][4 * g + 2], dkacc[db][4 * g + 3]};
+        red_v[(db * 4 + g) * 64] = f32x4{dvacc[db][4 * g], dvacc[db][4 * g + 1], dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]};
+        red_k[(db * 4 + g) * 64] = f32x4{dkacc[db][4 * g], dkacc[db][4 * g + 1], dkacc[db][4 * g + 2], dkacc[db][4 * g + 3]};
       }
     }
   }
@@ -949,7 +963,7 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
     for (int db = 0; db < G::NDB; ++db) {
       #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 x = red[ridx(0, db, g)], y = red[ridx(1, db, g)];
+        const f32x4 x = red_v[(db * 4 + g) * 64], y = red_k[(db * 4 + g) * 64];
         #pragma unroll
         for (int j = 0; j < 4; ++j) {
           dvacc[db][4 * g + j] += x[j];
@@ -959,10 +973,15 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
     }
   }
   __syncthreads();
-  // fp32 rows of dV and dK in LDS ([tensor][128 rows][D], 16-byte chunk c of
-  // row r at c xor (r mod 32)), then bf16 rows out by all eight waves
+  // fp32 rows of dV (in the key rows) and dK (rows 0..63 in stage 0, 64..127
+  // in stage 1) in LDS, 16-byte chunk c of row r at c xor (r mod 32), then
+  // bf16 rows out by all eight waves
   constexpr int OCPR = D / 4;
-  __attribute__((address_space(3))) float* ost = LDS_PTR(float, &sm);
+  using LFP = __attribute__((address_space(3))) float;
+  auto orow = [&](int t, int r) -> LFP* {
+    if (t == 0) return LDS_PTR(float, &kv) + r * D;
+    return LDS_PTR(float, r < 64 ? (void*)&st0 : (void*)&st1) + (r & 63) * D;
+  };
   if (qb == 0) {
     const float sv = -LN2 / (float)n_norm, sk = a.alpha / (float)n_norm;
     const int row_w = key_w;
@@ -971,10 +990,10 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
       #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c = (32 * db + 8 * g + 4 * hl) / 4;
-        const int off = row_w * D + (c ^ (row_w % OCPR)) * 4;
-        *(__attribute__((address_space(3))) f32x4*)(ost + off) =
+        const int off = (c ^ (row_w % OCPR)) * 4;
+        *(LF4*)(orow(0, row_w) + off) =
             f32x4{dvacc[db][4 * g] * sv, dvacc[db][4 * g + 1] * sv, dvacc[db][4 * g + 2] * sv, dvacc[db][4 * g + 3] * sv};
-        *(__attribute__((address_space(3))) f32x4*)(ost + QT * D + off) =
+        *(LF4*)(orow(1, row_w) + off) =
             f32x4{dkacc[db][4 * g] * sk, dkacc[db][4 * g + 1] * sk, dkacc[db][4 * g + 2] * sk, dkacc[db][4 * g + 3] * sk};
       }
     }
@@ -983,7 +1002,7 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
   for (int i = tid; i < 2 * QT * OCPR; i += DKDV8_THREADS) {
     const int t = i / (QT * OCPR), r = (i / OCPR) % QT, c = i % OCPR;
     if (r < klen) {
-      const f32x4 x = *(__attribute__((address_space(3))) const f32x4*)(ost + t * QT * D + r * D + (c ^ (r % OCPR)) * 4);
+      const f32x4 x = *(const LF4*)(orow(t, r) + (c ^ (r % OCPR)) * 4);
       const bf16x4 v = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
       *(bf16x4*)((bf16*)(t == 0 ? a.dv : a.dk) + ((q_off + k0 + r) * H + h) * D + c * 4) = v;
     }
