@@ -251,17 +251,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
       dop[s] = y;
     }
   }
-  uint32_t koff[G::NQOP], ktr[G::NDB][2];
-  {
-    const int kr = M::krow(0, l32);
-    #pragma unroll
-    for (int s = 0; s < G::NQOP; ++s) koff[s] = (uint32_t)b_off<D>(kr, 2 * s + hl);
-    #pragma unroll
-    for (int db = 0; db < G::NDB; ++db) {
-      ktr[db][0] = tr_off_b<D>(lane, db, 0, 0);
-      ktr[db][1] = tr_off_b<D>(lane, db, 0, 1);
-    }
-  }
+  // Operand offsets. K / V rows (A operand, in the order of M::krow): the
+  // chunk of step i of row r sits at r * ROWB + ((2i + hl) xor swz(r)) * 16
+  // = (r * ROWB + (hl xor swz(r)) * 16) xor 32i, since the row and chunk
+  // fields do not overlap. Transposing reads of d block db: the offset of
+  // block 0 xor 64db.
+  const int kr = M::krow(0, l32);
+  const uint32_t k_base = (uint32_t)(kr * G::ROWB + ((hl ^ swz_b<D>(kr)) << 4));
+  const uint32_t t_base0 = tr_off_b<D>(lane, 0, 0, 0), t_base1 = tr_off_b<D>(lane, 0, 0, 1);
   f32x16 dqacc[G::NDB];
   #pragma unroll
   for (int i = 0; i < G::NDB; ++i) dqacc[i] = f32x16{};
@@ -307,6 +304,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     const int32_t tsq_lo = (int32_t)tsq;
     LB* kl = LDS_PTR(unsigned char, st.k);
     LB* vl = LDS_PTR(unsigned char, st.v);
+    // the bases pass through an empty asm so that the offsets derived from
+    // them are formed here, in every tile, instead of being kept in registers
+    uint32_t kb_t = k_base, tb0 = t_base0, tb1 = t_base1;
+    asm volatile("" : "+v"(kb_t), "+v"(tb0), "+v"(tb1));
     float tile_sum = 0.0f;
     // General path: a lane's keys come in increasing order along v, so with
     // ordered timestamps its time bucket (and a clamped position bucket)
@@ -316,16 +317,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     float run_p = 0.0f, run_t = 0.0f;
     #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // S^T and dP^T as two interleaved chains, the K and V operands of step
+      // i + 1 read while the MFMAs of step i run
       f32x16 s = f32x16{}, dp = f32x16{};
+      bf16x8 op[2][2];
+      auto read_step = [&](int i, bf16x8* o) {
+        const uint32_t off = (kb_t ^ (uint32_t)(i << 5)) + kb * 32 * G::ROWB;
+        o[0] = *(__attribute__((address_space(3))) const bf16x8*)(kl + off);
+        o[1] = *(__attribute__((address_space(3))) const bf16x8*)(vl + off);
+      };
+      read_step(0, op[0]);
       #pragma unroll
       for (int i = 0; i < G::NQOP; ++i) {
-        const bf16x8 kop = *(__attribute__((address_space(3))) const bf16x8*)(kl + koff[i] + kb * 32 * G::ROWB);
-        s = M::run(kop, qop[i], s);
-      }
-      #pragma unroll
-      for (int i = 0; i < G::NQOP; ++i) {
-        const bf16x8 vop = *(__attribute__((address_space(3))) const bf16x8*)(vl + koff[i] + kb * 32 * G::ROWB);
-        dp = M::run(vop, dop[i], dp);
+        if (i + 1 < G::NQOP) read_step(i + 1, op[(i + 1) & 1]);
+        s = M::run(op[i & 1][0], qop[i], s);
+        dp = M::run(op[i & 1][1], dop[i], dp);
+        __builtin_amdgcn_sched_barrier(0);
       }
       bf16x8 dsb[2];
       if (fast) {
@@ -378,17 +385,28 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         if (small_span) general(std::true_type{});
         else general(std::false_type{});
       }
-      // dQ^T += K^T dS^T for the 32 keys of block kb
-      #pragma unroll
-      for (int db = 0; db < G::NDB; ++db) {
+      // dQ^T += K^T dS^T for the 32 keys of block kb, the transposed
+      // operands of d block db + 1 read during the MFMAs of block db
+      bf16x8 kt[2][2];
+      auto read_tr = [&](int db, bf16x8* o) {
         #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          const int o = (2 * kb + cc) * 16 * G::ROWB;
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(kl + ktr[db][0] + o));
-          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(kl + ktr[db][1] + o));
-          const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          dqacc[db] = M::run(kt, dsb[cc], dqacc[db]);
+          const int off = (2 * kb + cc) * 16 * G::ROWB;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(kl + (tb0 ^ (uint32_t)(db << 6)) + off));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(kl + (tb1 ^ (uint32_t)(db << 6)) + off));
+          o[cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
+      };
+      read_tr(0, kt[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      #pragma unroll
+      for (int db = 0; db < G::NDB; ++db) {
+        if (db + 1 < G::NDB) read_tr(db + 1, kt[(db + 1) & 1]);
+        #pragma unroll
+        for (int cc = 0; cc < 2; ++cc) dqacc[db] = M::run(kt[db & 1][cc], dsb[cc], dqacc[db]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (cur_p >= 0) lds_add_f32(&hist.pos[wave][cur_p], run_p);
