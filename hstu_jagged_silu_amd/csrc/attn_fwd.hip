@@ -252,11 +252,12 @@ void attn_fwd_kernel(AttnArgs a) {
   // Per-lane byte offsets of this lane's MFMA operand reads inside a stage's K
   // and V tiles, for key block 0 (the second 32-key block adds 32 rows, the
   // second 16-key half of a V operand 16 rows: compile-time offsets).
-  uint32_t koff[G::NQOP], voff[G::NDB][2];
+  // In bf16 the K chunk of step s of row r sits at r * ROWB + ((2s + hl) xor
+  // swz(r)) * 16 = (r * ROWB + (hl xor swz(r)) * 16) xor 32s (row and chunk
+  // fields do not overlap), so one base per lane serves every step.
+  uint32_t voff[G::NDB][2];
+  const uint32_t k_base = (uint32_t)G::k_off(M::krow(0, l32), sizeof(T) == 2 ? hl : 0);
   {
-    const int kr = M::krow(0, l32);
-    #pragma unroll
-    for (int s = 0; s < G::NQOP; ++s) koff[s] = (uint32_t)G::k_off(kr, sizeof(T) == 2 ? 2 * s + hl : 0);
     #pragma unroll
     for (int db = 0; db < G::NDB; ++db) {
       voff[db][0] = (uint32_t)v_tr_off(db, 0, 0);
@@ -364,15 +365,29 @@ void attn_fwd_kernel(AttnArgs a) {
     if constexpr (sizeof(T) == 2) {
       LB* kl = LDS_PTR(unsigned char, st.k);
       LB* vl = LDS_PTR(unsigned char, st.v);
-      // S^T = K Q^T for the 32 keys of block kb
-      auto s_chain = [&](int kb) {
-        f32x16 acc = f32x16{};
+      // S^T = K Q^T for both 32-key blocks as two interleaved chains, the K
+      // operands of step s + 1 read while the MFMAs of step s run; the base
+      // passes through an empty asm so that the step offsets are formed here,
+      // in every tile, instead of being kept in registers
+      auto s_chains = [&](f32x16& s0, f32x16& s1) {
+        uint32_t kb_t = k_base;
+        asm volatile("" : "+v"(kb_t));
+        s0 = f32x16{};
+        s1 = f32x16{};
+        bf16x8 op[2][2];
+        auto read_step = [&](int i, bf16x8* o) {
+          const uint32_t off = kb_t ^ (uint32_t)(i << 5);
+          o[0] = *(__attribute__((address_space(3))) const bf16x8*)(kl + off);
+          o[1] = *(__attribute__((address_space(3))) const bf16x8*)(kl + off + 32 * G::ROWB);
+        };
+        read_step(0, op[0]);
         #pragma unroll
-        for (int s = 0; s < G::NQOP; ++s) {
-          const bf16x8 kop = *(__attribute__((address_space(3))) const bf16x8*)(kl + koff[s] + kb * 32 * G::ROWB);
-          acc = M::run(kop, qop[s], acc);
+        for (int i = 0; i < G::NQOP; ++i) {
+          if (i + 1 < G::NQOP) read_step(i + 1, op[(i + 1) & 1]);
+          s0 = M::run(op[i & 1][0], qop[i], s0);
+          s1 = M::run(op[i & 1][1], qop[i], s1);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        return acc;
       };
       // O^T += V^T P^T for block kb; V^T operands from two transposing reads
       auto pv = [&](int kb, const bf16x8* pb) {
@@ -401,8 +416,8 @@ void attn_fwd_kernel(AttnArgs a) {
       // Score MFMAs of both 32-key blocks, then SiLU (one bias constant, or
       // per-element bias with the mask folded in), then the P V MFMAs. The
       // accumulators are only touched by code shared by every tile.
-      const f32x16 s0 = s_chain(0);
-      const f32x16 s1 = s_chain(1);
+      f32x16 s0, s1;
+      s_chains(s0, s1);
       bf16x8 p0[2], p1[2];
       if (uniform && !need_mask) {
         float cu[16];
