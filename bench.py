@@ -618,6 +618,9 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="time only the headline workload")
     ap.add_argument("--variants", default="", help="comma-separated subset of the variants to run (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock-read", action="store_true",
+                    help="skip the amd-smi clock reads (peak_sustained null); for counter runs, where the "
+                         "profiler's preloaded library makes every child process a GPU client")
     ap.add_argument("--cpu-sample-rows", type=int, default=8192)
     ap.add_argument("--cpu-sample-users", type=int, default=3)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -657,7 +660,8 @@ def main():
     log(f"step {ms:.4f} ms ({value:.1f} TFLOP/s), attention kernel {attn_ms:.4f} ms ({achieved:.1f} TFLOP/s), "
         f"scheduler {sched_ms:.4f} ms, epilogue {ln_ms:.4f} ms")
 
-    clock_mhz, clock_reads = sustained_clock(torch, step_fn)
+    clock_mhz, clock_reads = ((None, "skipped (--no-clock-read)") if args.no_clock_read
+                              else sustained_clock(torch, step_fn))
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     peak_sustained = None
     if clock_mhz is not None:

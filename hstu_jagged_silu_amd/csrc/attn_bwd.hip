@@ -23,6 +23,8 @@
 //     see them: S = Q K^T and dP = dO V^T (Q and dO rows from LDS, K and V in
 //     registers), then dV^T += dO^T P and dK^T += Q^T dS. The item of query
 //     tile t of a user maps to key block (tiles - 1 - t), whose cost matches.
+//     For d = 128, attn_bwd_dkdv8_kernel does the same work with eight waves
+//     (two per SIMD) and K and V held in LDS instead of registers.
 // A third kernel adds the per-item histograms in canonical item order.
 #include <type_traits>
 
