@@ -412,7 +412,7 @@ hstu_status_t hstu_attn_bwd(const hstu_params_t* params, int32_t batch, const in
   g.dv = grads->dv;
   g.rab_part = (float*)((char*)ws + w.rab_off);
   if (!mark(2)) return HSTU_ERR_LAUNCH;
-  if (!empty && launch_attn_bwd(g, params->head_dim, s.max_items, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  if (!empty && launch_attn_bwd(g, params->head_dim, s.max_items, max_len, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
   // 4. bias-table gradients
   RabReduceArgs r = {};
   r.part = g.rab_part;

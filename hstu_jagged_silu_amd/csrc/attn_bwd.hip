@@ -26,6 +26,8 @@
 //     For d = 128, attn_bwd_dkdv8_kernel does the same work with eight waves
 //     (two per SIMD) and K and V held in LDS instead of registers.
 // A third kernel adds the per-item histograms in canonical item order.
+#include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "tile.h"
@@ -466,6 +468,358 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     float x = 0.0f;
     #pragma unroll
     for (int w = 0; w < NWAVES; ++w) x += hist.time[w][tid];
+    part[BWD_MAX_NPOS + tid] = x * inv_n;
+  }
+}
+
+// ============================================================================
+// dQ and the bias-table gradients for d = 128: eight waves, two per SIMD
+// ============================================================================
+// Wave w owns the 32 rows of group w mod 4 against the key half w / 4 (32
+// keys) of every 64-key tile, with Q and dO of its rows in registers as in
+// the four-wave kernel; a wave's tile is half as long, so an item's chain of
+// tiles takes about half the time. The two halves' partial dQ sums are added
+// through LDS at the end, half 0 first; each wave keeps its own histograms,
+// added in wave order, so the result does not depend on wave timing.
+constexpr int DQ8_WAVES = 8;
+constexpr int DQ8_THREADS = 64 * DQ8_WAVES;
+// the end of the kernel reuses the two stages: the fp32 partial dQ of half 1
+// (2 row groups x 64 lanes x 64 floats per stage), then the fp32 dQ rows on
+// their way out (64 x 128 per stage)
+static_assert(sizeof(Stage<bf16, 128>) >= QT / 2 * 128 * 4, "reduction buffers");
+
+struct RabHist8 {
+  float pos[DQ8_WAVES][BWD_MAX_NPOS];
+  float time[DQ8_WAVES][64];
+};
+
+__global__ __launch_bounds__(DQ8_THREADS, 2) void attn_bwd_dq8_kernel(BwdArgs a) {
+  constexpr int D = 128;
+  using T = bf16;
+  using G = Geo<T, D>;
+  using M = Mfma<T>;
+  static_assert(G::ROWB == 256 && G::CPR == 16, "resident rows of 256 bytes");
+  __shared__ Stage<T, D> st0;  // k: K rows, v: V rows (both with swz_b)
+  __shared__ Stage<T, D> st1;
+  __shared__ BwdTables tab;
+  __shared__ RabHist8 hist;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qg = wave & 3, kh = wave >> 2;  // row group, key half
+  const int32_t count = ldc(a.count);
+  const WorkItem it = ldc(a.items + blockIdx.x);  // in bounds for every workgroup of the grid
+  if ((int64_t)blockIdx.x >= (int64_t)count) return;
+  const int b = it.b, h = it.h, q_start = it.q_start, q_len = it.q_len;
+  const int k_begin = it.k_begin, k_end = it.k_end;
+  const int H = a.H;
+  const int64_t q_off = it.off;
+  const int L = it.L;
+  const int n_norm = a.norm_n > 0 ? a.norm_n : L;
+  const int n_pos = a.pos_tab ? a.n_pos : 1;
+  load_bwd_tables<DQ8_THREADS>(a, h, tab, n_pos);
+  for (int i = tid; i < DQ8_WAVES * BWD_MAX_NPOS; i += DQ8_THREADS) (&hist.pos[0][0])[i] = 0.0f;
+  for (int i = tid; i < DQ8_WAVES * 64; i += DQ8_THREADS) (&hist.time[0][0])[i] = 0.0f;
+
+  const int row_w = qg * 32 + l32;
+  const bool row_ok = row_w < q_len;
+  const int row_c = min(row_w, q_len - 1);
+  const int64_t qrow = q_off + q_start + row_c;
+  const int p_lane = q_start + row_c;
+  const int64_t tsq = a.ts[qrow];
+  const int w_first = qg * 32;
+  const bool w_rows = w_first < q_len;
+  const int w_last = min(w_first + 31, q_len - 1);
+  const int w_lim_min = q_start + w_first, w_lim_max = q_start + w_last;
+  int64_t w_ts_min = row_ok ? tsq : INT64_MAX, w_ts_max = row_ok ? tsq : INT64_MIN;
+  for (int m = 32; m >= 1; m >>= 1) {
+    w_ts_min = min(w_ts_min, shfl_xor64(w_ts_min, m));
+    w_ts_max = max(w_ts_max, shfl_xor64(w_ts_max, m));
+  }
+  w_ts_min = uniform64(w_ts_min);
+  w_ts_max = uniform64(w_ts_max);
+
+  // Q and dO rows of this lane as MFMA B operands (zero past the item's end,
+  // so those rows' dP, and with it their dS', is zero)
+  bf16x8 qop[G::NQOP], dop[G::NQOP];
+  {
+    const T* qp = (const T*)a.q + (qrow * H + h) * D;
+    const T* gp = (const T*)a.dout + (qrow * H + h) * D;
+    #pragma unroll
+    for (int i = 0; i < G::NQOP; ++i) {
+      bf16x8 x = *(const bf16x8*)(qp + 16 * i + 8 * hl);
+      bf16x8 y = *(const bf16x8*)(gp + 16 * i + 8 * hl);
+      if (!row_ok) { x = bf16x8{}; y = bf16x8{}; }
+      qop[i] = x;
+      dop[i] = y;
+    }
+  }
+
+  // Operand offsets (the chunk of step i of row r sits at (r * 256 + (hl xor
+  // swz(r)) * 16) xor 32i): K / V rows of this key half (A operand, rows in
+  // the order of M::krow), and the transposing K reads of d block db (the
+  // offset of block 0 xor 64db).
+  const int kr = M::krow(0, l32) + 32 * kh;
+  const uint32_t k_base = (uint32_t)(kr * G::ROWB + ((hl ^ swz_b<D>(kr)) << 4));
+  const uint32_t t_base0 = tr_off_b<D>(lane, 0, 0, 0) + kh * 32 * G::ROWB;
+  const uint32_t t_base1 = tr_off_b<D>(lane, 0, 0, 1) + kh * 32 * G::ROWB;
+  f32x16 dqacc[G::NDB];
+  #pragma unroll
+  for (int i = 0; i < G::NDB; ++i) dqacc[i] = f32x16{};
+  const float sc = a.alpha * -LOG2E;
+  const bool has_time = a.time_tab != nullptr;
+  const int n_time_eff = has_time ? min(a.n_time, 64) : 1;
+  using LB = __attribute__((address_space(3))) unsigned char;
+  using LV = __attribute__((address_space(3))) const bf16x8;
+  using LT = __attribute__((address_space(3))) v4i16;
+
+  auto key_time_range = [&](int j0, int64_t& kmin, int64_t& kmax) {
+    const int64_t r0 = q_off + j0;
+    const int64_t i0 = min(r0 / KT, a.n_stat_blocks - 1), i1 = min((r0 + KT - 1) / KT, a.n_stat_blocks - 1);
+    kmin = min(ldc(a.tstats + 2 * i0), ldc(a.tstats + 2 * i1));
+    kmax = max(ldc(a.tstats + 2 * i0 + 1), ldc(a.tstats + 2 * i1 + 1));
+    if (kmin > kmax) kmin = kmax = w_ts_min;
+  };
+
+  auto compute_tile = [&](Stage<T, D>& st, int j0) {
+    const int jh = j0 + 32 * kh;  // first key of this half
+    if (!w_rows || jh > w_lim_max) return;
+    const bool need_mask = jh + 31 > w_lim_min;
+    // one bias constant for the whole wave tile?
+    const bool pos_uniform = (a.pos_tab == nullptr) || (w_lim_min - (jh + 31) >= n_pos - 1);
+    bool time_uniform = !has_time;
+    int z_tile = 63;
+    bool small_span = true;
+    if (has_time) {
+      int64_t k_min, k_max;
+      key_time_range(j0, k_min, k_max);
+      const int64_t d1 = w_ts_max - k_min, d2 = k_max - w_ts_min;
+      small_span = max(d1 < 0 ? -d1 : d1, d2 < 0 ? -d2 : d2) < ((int64_t)1 << 31) - 2;
+      int64_t lo = -1, hi = -1;
+      if (w_ts_min >= k_max) { lo = w_ts_min - k_max; hi = w_ts_max - k_min; }
+      else if (k_min >= w_ts_max) { lo = k_min - w_ts_max; hi = k_max - w_ts_min; }
+      if (lo >= 0) {
+        const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
+        if (min(63 - zlo, n_time_eff - 1) == min(63 - zhi, n_time_eff - 1)) { time_uniform = true; z_tile = zlo; }
+      }
+    }
+    const bool fast = pos_uniform && time_uniform && !need_mask;
+    const float c_uni = (a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f) + (has_time ? tab.time_t[z_tile] : 0.0f);
+    const int lim_rel = p_lane - j0 - M::HLK * hl;  // key_of(kh, v, 0) <= lim_rel: allowed
+    const int64_t* ts_l = st.ts64 + M::HLK * hl;
+    const int32_t* tsl_lo = st.ts_lo + M::HLK * hl;
+    const int32_t tsq_lo = (int32_t)tsq;
+    LB* kl = LDS_PTR(unsigned char, st.k);
+    LB* vl = LDS_PTR(unsigned char, st.v);
+    // the bases pass through an empty asm so that the offsets derived from
+    // them are formed here, in every tile, instead of being kept in registers
+    uint32_t kb_t = k_base, tb0 = t_base0, tb1 = t_base1;
+    asm volatile("" : "+v"(kb_t), "+v"(tb0), "+v"(tb1));
+
+    // S^T = K Q^T and dP^T = V dO^T as two interleaved chains, the K and V
+    // operands of step i + 1 read while the MFMAs of step i run
+    f32x16 s = f32x16{}, dp = f32x16{};
+    bf16x8 op[2][2];
+    auto read_step = [&](int i, bf16x8* o) {
+      const uint32_t ko = kb_t ^ (uint32_t)(i << 5);
+      o[0] = *(LV*)(kl + ko);
+      o[1] = *(LV*)(vl + ko);
+    };
+    read_step(0, op[0]);
+    #pragma unroll
+    for (int i = 0; i < G::NQOP; ++i) {
+      if (i + 1 < G::NQOP) read_step(i + 1, op[(i + 1) & 1]);
+      s = M::run(op[i & 1][0], qop[i], s);
+      dp = M::run(op[i & 1][1], dop[i], dp);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    bf16x8 dsb[2];
+    if (fast) {
+      float tile_sum = 0.0f;
+      #pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float p, ds;
+        silu_fwd_bwd(fmaf(s[v], sc, c_uni), dp[v], p, ds);
+        tile_sum += ds;
+        dsb[v >> 3][v & 7] = (bf16)ds;
+      }
+      // rows past q_len have zero dO, so their dS' is 0 and they add nothing
+      const float tot = wave_sum_f(tile_sum);
+      if (lane == 0) {
+        if (a.pos_tab) hist.pos[wave][n_pos - 1] += tot;
+        if (has_time) hist.time[wave][min(63 - z_tile, n_time_eff - 1)] += tot;
+      }
+    } else {
+      // a lane's keys come in increasing order along v, so with ordered
+      // timestamps its time bucket (and a clamped position bucket) stays the
+      // same over runs of keys: dS' is summed per run and added to the
+      // wave's histogram when the bucket changes, not once per pair
+      int cur_p = -1, cur_t = -1;
+      float run_p = 0.0f, run_t = 0.0f;
+      auto general = [&](auto small_tag) {
+        constexpr bool SMALL = decltype(small_tag)::value;
+        #pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kk = M::key_of(kh, v, 0);
+          const bool ok = kk <= lim_rel;
+          const int rel = lim_rel - kk;  // query position - key position
+          const int pb = min((unsigned)rel, (unsigned)(n_pos - 1));
+          float cb = a.pos_tab ? tab.pos_t[pb] : 0.0f;
+          int tb = 0;
+          if (has_time) {
+            const int zc = time_z<SMALL>(tsq, SMALL ? 0 : ts_l[kk], tsq_lo, SMALL ? tsl_lo[kk] : 0);
+            cb += tab.time_t[zc];
+            tb = min(63 - zc, n_time_eff - 1);
+          }
+          float p, ds;
+          silu_fwd_bwd(ok ? fmaf(s[v], sc, cb) : MASKED_Y, dp[v], p, ds);
+          dsb[v >> 3][v & 7] = (bf16)ds;
+          if (ok && row_ok) {
+            if (a.pos_tab) {
+              if (pb != cur_p) {
+                if (cur_p >= 0) lds_add_f32(&hist.pos[wave][cur_p], run_p);
+                cur_p = pb;
+                run_p = 0.0f;
+              }
+              run_p += ds;
+            }
+            if (has_time) {
+              if (tb != cur_t) {
+                if (cur_t >= 0) lds_add_f32(&hist.time[wave][cur_t], run_t);
+                cur_t = tb;
+                run_t = 0.0f;
+              }
+              run_t += ds;
+            }
+          }
+        }
+      };
+      if (small_span) general(std::true_type{});
+      else general(std::false_type{});
+      if (cur_p >= 0) lds_add_f32(&hist.pos[wave][cur_p], run_p);
+      if (cur_t >= 0) lds_add_f32(&hist.time[wave][cur_t], run_t);
+    }
+
+    // dQ^T += K^T dS^T for the 32 keys of this half, the transposed operands
+    // of d block db + 1 read during the MFMAs of block db
+    bf16x8 kt[2][2];
+    auto read_tr = [&](int db, bf16x8* o) {
+      #pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const uint32_t o0 = (tb0 ^ (uint32_t)(db << 6)) + cc * 16 * G::ROWB;
+        const uint32_t o1 = (tb1 ^ (uint32_t)(db << 6)) + cc * 16 * G::ROWB;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(kl + o0));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(kl + o1));
+        o[cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    read_tr(0, kt[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+      if (db + 1 < G::NDB) read_tr(db + 1, kt[(db + 1) & 1]);
+      #pragma unroll
+      for (int cc = 0; cc < 2; ++cc) dqacc[db] = M::run(kt[db & 1][cc], dsb[cc], dqacc[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  const int ntiles = k_end > k_begin ? (int)ceil_div(k_end - k_begin, KT) : 0;
+  int64_t tsreg = 0;
+  auto issue = [&](Stage<T, D>& st, int j0) {
+    stage_rows<D, DQ8_WAVES>(a, a.k, a.v, st, q_off + j0, min(KT, L - j0), h, tsreg);
+  };
+  if (ntiles > 0) {
+    issue(st0, k_begin);
+    finish_stage<D>(st0, tsreg);  // also orders the tables and histograms
+  } else {
+    __syncthreads();
+  }
+  for (int t = 0; t < ntiles; t += 2) {
+    const int j0 = k_begin + t * KT;
+    if (t + 1 < ntiles) issue(st1, j0 + KT);
+    compute_tile(st0, j0);
+    if (t + 1 >= ntiles) break;
+    finish_stage<D>(st1, tsreg);
+    if (t + 2 < ntiles) issue(st0, j0 + 2 * KT);
+    compute_tile(st1, j0 + KT);
+    if (t + 2 < ntiles) finish_stage<D>(st0, tsreg);
+  }
+
+  // half 1 hands its partial dQ to half 0 ([group][db][4][lane] x f32x4,
+  // groups 0, 1 in stage 0 and 2, 3 in stage 1), then the fp32 rows go out as
+  // bf16 through the same space
+  __syncthreads();
+  using LF4 = __attribute__((address_space(3))) f32x4;
+  LF4* red = LDS_PTR(f32x4, qg < 2 ? (void*)&st0 : (void*)&st1) + (qg & 1) * (G::NDB * 4 * 64) + lane;
+  if (kh == 1) {
+    #pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+      #pragma unroll
+      for (int g = 0; g < 4; ++g)
+        red[(db * 4 + g) * 64] = f32x4{dqacc[db][4 * g], dqacc[db][4 * g + 1], dqacc[db][4 * g + 2], dqacc[db][4 * g + 3]};
+    }
+  }
+  __syncthreads();
+  if (kh == 0) {
+    #pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+      #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = red[(db * 4 + g) * 64];
+        #pragma unroll
+        for (int j = 0; j < 4; ++j) dqacc[db][4 * g + j] += x[j];
+      }
+    }
+  }
+  __syncthreads();
+  // fp32 rows 0..63 in stage 0 and 64..127 in stage 1, chunk c of row r at c xor (r mod 32)
+  constexpr int OCPR = D / 4;
+  using LFP = __attribute__((address_space(3))) float;
+  auto orow = [&](int r) -> LFP* { return LDS_PTR(float, r < 64 ? (void*)&st0 : (void*)&st1) + (r & 63) * D; };
+  if (kh == 0) {
+    const float sq = a.alpha / (float)n_norm;
+    #pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+      #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = (32 * db + 8 * g + 4 * hl) / 4;
+        *(LF4*)(orow(row_w) + (c ^ (row_w % OCPR)) * 4) =
+            f32x4{dqacc[db][4 * g] * sq, dqacc[db][4 * g + 1] * sq, dqacc[db][4 * g + 2] * sq, dqacc[db][4 * g + 3] * sq};
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < QT * OCPR; i += DQ8_THREADS) {
+    const int r = i / OCPR, c = i % OCPR;
+    if (r < q_len) {
+      const f32x4 x = *(const LF4*)(orow(r) + (c ^ (r % OCPR)) * 4);
+      const bf16x4 v = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+      *(bf16x4*)((bf16*)a.dq + ((q_off + q_start + r) * H + h) * D + c * 4) = v;
+    }
+  }
+
+  // per-item bias gradients (scaled by 1 / N), head-major: the items of head h
+  // are [h * tiles, (h + 1) * tiles), tiles = query tiles over all users
+  // (the scheduler's prefix counts H items per tile); waves added in order
+  const int64_t tiles = ldc(a.prefix + a.B) / H;
+  const int64_t canon = (int64_t)h * tiles + ldc(a.prefix + b) / H + q_start / QT;
+  float* part = a.rab_part + canon * RAB_SLOTS;
+  const float inv_n = 1.0f / (float)n_norm;
+  if (a.pos_tab) {
+    for (int i = tid; i < n_pos; i += DQ8_THREADS) {
+      float x = 0.0f;
+      #pragma unroll
+      for (int w = 0; w < DQ8_WAVES; ++w) x += hist.pos[w][i];
+      part[i] = x * inv_n;
+    }
+  }
+  if (has_time && tid < 64) {
+    float x = 0.0f;
+    #pragma unroll
+    for (int w = 0; w < DQ8_WAVES; ++w) x += hist.time[w][tid];
     part[BWD_MAX_NPOS + tid] = x * inv_n;
   }
 }
@@ -1074,11 +1428,28 @@ __global__ __launch_bounds__(64 * RAB_GROUPS) void rab_reduce_kernel(RabReduceAr
   }
 }
 
-hipError_t launch_attn_bwd(const BwdArgs& a, int D, int64_t grid, hipStream_t s) {
+// Which dQ kernel for d = 128. Measured on 8 x 8,192 and on the jagged
+// training shape, the eight-wave kernel (one workgroup per CU) costs about
+// 1.22x the four-wave one (two per CU) per unit of work, but finishes an
+// item's chain of key tiles in about 0.6x the time. So it wins when the
+// longest chain, not the total work, sets the launch's time: with W the work
+// in 128-row x 64-key tiles and C the longest chain in key tiles, when
+// W / 512 < 0.82 C, i.e. W < 420 C. W is estimated from what the host knows,
+// max(T^2 / B, max_len^2) * H / (128 * 64) (the first term is exact for equal
+// lengths, the second for one long user); C = ceil(max_len / 64).
+bool bwd_dq_eight_waves(const BwdArgs& a, int max_len) {
+  const double T = (double)a.T, B = (double)std::max(1, a.B), L = (double)max_len;
+  const double work = std::max(T * T / B, L * L) * a.H / (double)(QT * KT);
+  const double chain = std::ceil(L / KT);
+  return work < 400.0 * chain;
+}
+
+hipError_t launch_attn_bwd(const BwdArgs& a, int D, int64_t grid, int max_len, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid), blk(NTHREADS);
   if (D == 128) {
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, g, blk, 0, s, a);
+    if (bwd_dq_eight_waves(a, max_len)) hipLaunchKernelGGL(attn_bwd_dq8_kernel, g, dim3(DQ8_THREADS), 0, s, a);
+    else hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, g, blk, 0, s, a);
     hipLaunchKernelGGL(attn_bwd_dkdv8_kernel, g, dim3(DKDV8_THREADS), 0, s, a);
   } else if (D == 64) {
     hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, g, blk, 0, s, a);

@@ -204,7 +204,9 @@ hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int mode, int64_t gr
 hipError_t launch_ln_gate(const LnArgs& a, int dtype, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_ln_bwd(const LnBwdArgs& a, hipStream_t s);       // rows, then the affine reduce
-hipError_t launch_attn_bwd(const BwdArgs& a, int D, int64_t grid, hipStream_t s);
+hipError_t launch_attn_bwd(const BwdArgs& a, int D, int64_t grid, int max_len, hipStream_t s);
+// true when d = 128 takes the eight-wave dQ kernel (latency-bound launches)
+bool bwd_dq_eight_waves(const BwdArgs& a, int max_len);
 hipError_t launch_rab_reduce(const RabReduceArgs& a, hipStream_t s);
 
 }  // namespace hstu

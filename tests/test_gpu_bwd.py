@@ -105,6 +105,19 @@ def test_training_shape_config():
     check(g, ref, label="training shape")
 
 
+def test_wide_batch_four_wave_dq():
+    """64 users of up to 512 tokens, 2 x 128: a launch bound by its total work
+    (estimated max(T^2 / B, max_len^2) * H / (128 * 64) = 3,843 tiles against
+    400 x a longest chain of 8 key tiles), so d = 128 takes the four-wave dQ
+    kernel; the smaller d = 128 cases here take the eight-wave one."""
+    inp = W.jagged("bwd_wide", 85, [512] * 60 + [500, 384, 130, 7], 2, 128, "bf16", 128, 128)
+    T, B, L, H = inp.total, 64, inp.max_len, 2
+    assert max(T * T / B, L * L) * H / (128 * 64) >= 400 * -(-L // 64)
+    dy = W.upstream_grad(86, inp.u.shape)
+    g, ref = run_bwd(inp, dy, affine=W.affine_terms(87, 256))
+    check(g, ref, label="64 users, four-wave dQ")
+
+
 def test_repeat_is_bitwise_and_workspace_reuse():
     inp = W.jagged("bwd_rep", 71, [333, 64, 512], 2, 128, "bf16", 128, 128)
     dy = W.upstream_grad(72, inp.u.shape)
