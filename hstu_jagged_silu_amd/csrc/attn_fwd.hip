@@ -267,33 +267,70 @@ void attn_fwd_kernel(AttnArgs a) {
 
   using LB = __attribute__((address_space(3))) unsigned char;
 
-  auto compute_tile = [&](Stage<T, D>& st, int j0) {
+  // Time-bias constant of each key tile for this wave, 64 tiles at a time
+  // (lane i holds tile t0 + i): the table value when every pair of the wave
+  // tile falls in one time bucket (ordered timestamps whose |dt| range stays
+  // inside one power of two, or the clamped last bucket), NaN where the
+  // bucket varies. One lane-parallel pass replaces a per-tile scalar
+  // classification (range loads, 64-bit compares, clz, table read).
+  float tc = 0.0f;
+  auto time_batch = [&](int t0, int ntiles) {
+    const int t = t0 + lane;
+    float c = __builtin_nanf("");
+    if (t < ntiles) {
+      const int j0 = k_begin + t * KT;
+      int64_t kmin, kmax;
+      if (mode_paged(MODE)) {
+        const int64_t blk = (int64_t)b * a.stat_stride + min(j0 / KT, a.stat_stride - 1);
+        kmin = a.tstats[2 * blk];
+        kmax = a.tstats[2 * blk + 1];
+      } else {
+        const int64_t r0 = q_off + j0;
+        const int64_t i0 = min(r0 / KT, a.n_stat_blocks - 1), i1 = min((r0 + KT - 1) / KT, a.n_stat_blocks - 1);
+        kmin = min(a.tstats[2 * i0], a.tstats[2 * i1]);
+        kmax = max(a.tstats[2 * i0 + 1], a.tstats[2 * i1 + 1]);
+      }
+      if (kmin > kmax) kmin = kmax = w_ts_min;  // no valid key: the bias value is irrelevant
+      int64_t lo = -1, hi = 0;
+      if (w_ts_min >= kmax) { lo = w_ts_min - kmax; hi = w_ts_max - kmin; }
+      else if (kmin >= w_ts_max) { lo = kmin - w_ts_max; hi = kmax - w_ts_min; }
+      if (lo >= 0) {
+        const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
+        const int blo = min(63 - zlo, n_time_eff - 1), bhi = min(63 - zhi, n_time_eff - 1);
+        if (blo == bhi) c = tab.time_t[zlo];
+      }
+    }
+    tc = c;
+  };
+
+  auto compute_tile = [&](Stage<T, D>& st, int j0, int t) {
     if (!w_rows || j0 > w_lim_max) return;  // every pair of this wave masked
 
     // classify the wave tile: mask, constant bias, or per-element bias
     const bool need_mask = j0 + KT - 1 > w_lim_min;
-    int64_t k_min = 0, k_max = 0;
-    if (has_time) key_time_range(j0, k_min, k_max);
     const bool pos_uniform = (a.pos_tab == nullptr) || (w_p_min - (j0 + KT - 1) >= n_pos - 1);
     bool time_uniform = !has_time;
     float c_time = 0.0f;
-    int64_t span_hi = 0;
     if (has_time) {
-      int64_t lo, hi;
-      bool ordered = true;
-      if (w_ts_min >= k_max) { lo = w_ts_min - k_max; hi = w_ts_max - k_min; }
-      else if (k_min >= w_ts_max) { lo = k_min - w_ts_max; hi = k_max - w_ts_min; }
-      else { ordered = false; lo = 0; hi = max(w_ts_max - k_min, k_max - w_ts_min); }
-      span_hi = hi;
-      if (ordered) {
-        const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
-        const int blo = min(63 - zlo, n_time_eff - 1), bhi = min(63 - zhi, n_time_eff - 1);
-        if (blo == bhi) { time_uniform = true; c_time = tab.time_t[zlo]; }
-      }
+      const float ct = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tc), t & 63));
+      time_uniform = ct == ct;  // NaN: the bucket varies over the tile
+      c_time = time_uniform ? ct : 0.0f;
     }
     const bool uniform = pos_uniform && time_uniform;
     const float c_pos = a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f;
-    const bool small_span = span_hi < ((int64_t)1 << 31) - 2;
+    // the keys' time range and |dt| span, needed only where the time bucket
+    // varies (per-element path)
+    int64_t k_min = 0, k_max = 0;
+    bool small_span = true;
+    auto load_time_range = [&]() {
+      if (time_uniform) return;
+      key_time_range(j0, k_min, k_max);
+      int64_t hi;
+      if (w_ts_min >= k_max) hi = w_ts_max - k_min;
+      else if (k_min >= w_ts_max) hi = k_max - w_ts_min;
+      else hi = max(w_ts_max - k_min, k_max - w_ts_min);
+      small_span = hi < ((int64_t)1 << 31) - 2;
+    };
     const int32_t tsq_lo = (int32_t)tsq;
     // per-lane bases: the per-register offsets key_of(kb, v, 0) are constants
     const int lim_rel = lim_lane - j0 - M::HLK * hl;   // allowed iff key_of(kb, v, 0) <= lim_rel
@@ -426,6 +463,7 @@ void attn_fwd_kernel(AttnArgs a) {
         silu_pack(s0, cu, p0);
         silu_pack(s1, cu, p1);
       } else {
+        load_time_range();
         float cb[16];
         element_bias(0, cb, true);
         silu_pack(s0, cb, p0);
@@ -437,6 +475,7 @@ void attn_fwd_kernel(AttnArgs a) {
     } else {
       const unsigned char* kl = st.k;
       const unsigned char* vl = st.v;
+      if (!uniform) load_time_range();
       #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float acc_p[16];
@@ -485,13 +524,16 @@ void attn_fwd_kernel(AttnArgs a) {
     __syncthreads();  // tables
   }
   for (int t = 0; t < ntiles; t += 2) {
+    // the next 64 tiles' time classes: loads issued before this step's DMA,
+    // so waiting for them does not wait for the DMA
+    if (has_time && (t & 63) == 0) time_batch(t, ntiles);
     const int j0 = k_begin + t * KT;
     if (t + 1 < ntiles) issue_tile(st1, j0 + KT);
-    compute_tile(st0, j0);
+    compute_tile(st0, j0, t);
     if (t + 1 >= ntiles) break;
     finish_tile(st1);
     if (t + 2 < ntiles) issue_tile(st0, j0 + 2 * KT);
-    compute_tile(st1, j0 + KT);
+    compute_tile(st1, j0 + KT, t + 1);
     if (t + 2 < ntiles) finish_tile(st0);
   }
 
