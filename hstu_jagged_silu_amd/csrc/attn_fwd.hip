@@ -191,15 +191,18 @@ void attn_fwd_kernel(AttnArgs a) {
         *(i32x4*)(st.v + P * 16) = i32x4{};
       }
     } else {
+      // a lane's source is the tile's base (wave-uniform) plus a 32-bit
+      // offset: at most 63 rows of H * D <= 2048 elements (a 24-bit product)
+      const uint32_t rs32 = (uint32_t)rstride;
       #pragma unroll
       for (int i = 0; i < G::NDMA; ++i) {
         const int base = (wave * G::NDMA + i) * 64;      // first LDS chunk of this instruction
         const int P = base + lane;
         const int r = P / G::CPR, pc = P % G::CPR;
-        const int64_t row = min(r, last) * rstride;
-        __builtin_amdgcn_global_load_lds((const void*)(kbase + row + ((pc ^ G::swz_k(r)) << 4)),
+        const uint32_t row = __umul24((uint32_t)min(r, last), rs32);
+        __builtin_amdgcn_global_load_lds((const void*)(kbase + (row + (uint32_t)((pc ^ G::swz_k(r)) << 4))),
                                          LDS_PTR(void, st.k + base * 16), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vbase + row + ((pc ^ G::swz_v(r)) << 4)),
+        __builtin_amdgcn_global_load_lds((const void*)(vbase + (row + (uint32_t)((pc ^ G::swz_v(r)) << 4))),
                                          LDS_PTR(void, st.v + base * 16), 16, 0, 0);
       }
     }
