@@ -155,6 +155,11 @@ void attn_fwd_kernel(AttnArgs a) {
   // valid row: finite values that the causal mask zeroes. A missing page of
   // the cached path reads as zeros.
   int64_t tsreg = 0;
+  // full path: the item's K, V and timestamp rows start at the user's first
+  // row; rows_left rows of the buffer exist from there on
+  const int rows_left = (int)min<int64_t>(a.Tq - q_off, (int64_t)INT_MAX);
+  const unsigned char* k_item = (const unsigned char*)a.k + ((q_off * H + h) * D) * (int64_t)sizeof(T);
+  const unsigned char* v_item = (const unsigned char*)a.v + ((q_off * H + h) * D) * (int64_t)sizeof(T);
 
   auto issue_tile = [&](Stage<T, D>& st, int j0) {
     const unsigned char* kbase;
@@ -175,12 +180,13 @@ void attn_fwd_kernel(AttnArgs a) {
       rstride = G::ROWB;
       tsbase = a.ts_pages + (int64_t)page * PAGE;
     } else {
-      const int64_t r0 = min(q_off + j0, a.Tq - 1);
-      nvalid = (int)min<int64_t>(nvalid, a.Tq - r0);
-      kbase = (const unsigned char*)a.k + ((r0 * H + h) * D) * (int64_t)sizeof(T);
-      vbase = (const unsigned char*)a.v + ((r0 * H + h) * D) * (int64_t)sizeof(T);
+      // row q_off + jr = min(q_off + j0, Tq - 1), in 32-bit arithmetic
+      const int jr = min(j0, rows_left - 1);
+      nvalid = min(nvalid, rows_left - jr);
       rstride = (int64_t)H * G::ROWB;
-      tsbase = a.ts + r0;
+      kbase = k_item + (int64_t)jr * rstride;
+      vbase = v_item + (int64_t)jr * rstride;
+      tsbase = a.ts + (q_off + jr);
     }
     const int last = max(nvalid - 1, 0);
     if (missing) {
