@@ -449,36 +449,48 @@ void attn_fwd_kernel(AttnArgs a) {
           }
         }
       };
-      // SiLU with y = s * (-alpha log2 e) + bias, packed to bf16
-      auto silu_pack = [&](const f32x16& acc, const float* cb, bf16x8* pb) {
+      // SiLU of y = s * (-alpha log2 e) + bias, packed to bf16
+      auto silu_pack = [&](const float* y, bf16x8* pb) {
         #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float y = fmaf(acc[v], sc, cb[v]);
-          const float p = y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
+          const float p = y[v] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y[v]));
           pb[v >> 3][v & 7] = (bf16)p;
         }
       };
 
-      // Score MFMAs of both 32-key blocks, then SiLU (one bias constant, or
-      // per-element bias with the mask folded in), then the P V MFMAs. The
-      // accumulators are only touched by code shared by every tile.
+      // Score MFMAs of both 32-key blocks, then the biased scores y (one bias
+      // constant, or per-element bias with the mask folded in), then SiLU and
+      // the P V MFMAs. The accumulators and the SiLU are only touched by code
+      // shared by every tile; the empty asm keeps each kind's bias FMAs in its
+      // own branch, so that the shared code does not take a 16-value bias
+      // (which the constant kind would fill with 16 register copies per tile).
       f32x16 s0, s1;
       s_chains(s0, s1);
-      bf16x8 p0[2], p1[2];
+      float y0[16], y1[16];
       if (uniform && !need_mask) {
-        float cu[16];
+        const float cu = c_pos + c_time;
         #pragma unroll
-        for (int v = 0; v < 16; ++v) cu[v] = c_pos + c_time;
-        silu_pack(s0, cu, p0);
-        silu_pack(s1, cu, p1);
+        for (int v = 0; v < 16; ++v) {
+          y0[v] = fmaf(s0[v], sc, cu);
+          y1[v] = fmaf(s1[v], sc, cu);
+          asm volatile("" : "+v"(y0[v]), "+v"(y1[v]));
+        }
       } else {
         load_time_range();
         float cb[16];
         element_bias(0, cb, true);
-        silu_pack(s0, cb, p0);
+        #pragma unroll
+        for (int v = 0; v < 16; ++v) y0[v] = fmaf(s0[v], sc, cb[v]);
         element_bias(1, cb, true);
-        silu_pack(s1, cb, p1);
+        #pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          y1[v] = fmaf(s1[v], sc, cb[v]);
+          asm volatile("" : "+v"(y0[v]), "+v"(y1[v]));
+        }
       }
+      bf16x8 p0[2], p1[2];
+      silu_pack(y0, p0);
+      silu_pack(y1, p1);
       pv(0, p0);
       pv(1, p1);
     } else {
