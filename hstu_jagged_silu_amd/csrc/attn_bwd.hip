@@ -48,6 +48,44 @@ __device__ inline int time_z(int64_t ta, int64_t tb, int32_t ta_lo, int32_t tb_l
   }
 }
 
+// Time class of a wave tile: the other side's timestamp range [o_min, o_max]
+// (keys for dQ, queries for dK / dV; an empty range is replaced by the
+// wave's own minimum) against the wave's own [w_min, w_max]. Bits 0..6:
+// z = clz64(|dt| + 1) when every pair of the tile falls in one (clamped)
+// time bucket, else 127; bit 7: every |dt| stays below 2^31 - 2, so the
+// 32-bit bucket form is exact. A wave computes it for 64 tiles at a time,
+// lane i for tile t0 + i, and each tile reads its class with one readlane.
+__device__ inline int time_class(int64_t o_min, int64_t o_max, int64_t w_min, int64_t w_max, int n_time_eff) {
+  if (o_min > o_max) o_min = o_max = w_min;
+  const int64_t d1 = w_max - o_min, d2 = o_max - w_min;
+  const bool small = max(d1 < 0 ? -d1 : d1, d2 < 0 ? -d2 : d2) < ((int64_t)1 << 31) - 2;
+  int z = 127;
+  int64_t lo = -1, hi = -1;
+  if (w_min >= o_max) { lo = w_min - o_max; hi = w_max - o_min; }
+  else if (o_min >= w_max) { lo = o_min - w_max; hi = o_max - w_min; }
+  if (lo >= 0) {
+    const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
+    if (min(63 - zlo, n_time_eff - 1) == min(63 - zhi, n_time_eff - 1)) z = zlo;
+  }
+  return (small ? 128 : 0) | z;
+}
+
+// Timestamp range (conservative superset) of the packed rows r0 .. r0 + 63,
+// from the per-64-row-block ranges the scheduler wrote; per lane.
+__device__ inline void row_time_range(const BwdArgs& a, int64_t r0, int64_t& mn, int64_t& mx) {
+  const int64_t i0 = min(r0 / KT, a.n_stat_blocks - 1), i1 = min((r0 + KT - 1) / KT, a.n_stat_blocks - 1);
+  mn = min(a.tstats[2 * i0], a.tstats[2 * i1]);
+  mx = max(a.tstats[2 * i0 + 1], a.tstats[2 * i1 + 1]);
+}
+
+// Unpacks a tile's time class (see time_class) for the wave-uniform tile t.
+__device__ inline void tile_class(int tcls, int t, bool& time_uniform, int& z_tile, bool& small_span) {
+  const int c = __builtin_amdgcn_readlane(tcls, t & 63);
+  small_span = c >= 128;
+  time_uniform = (c & 127) != 127;
+  if (time_uniform) z_tile = c & 127;
+}
+
 struct BwdTables {
   float pos_t[BWD_MAX_NPOS];  // -log2(e) * position table
   float time_t[64];           // -log2(e) * time table, indexed by clz64(|dt| + 1)
@@ -135,7 +173,9 @@ __device__ inline void stage_rows(const BwdArgs& a, const void* x0, const void* 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int last = max(nvalid - 1, 0);
-  const int64_t rstride = (int64_t)a.H * G::ROWB;
+  // a lane's source is the tile's base (wave-uniform) plus a 32-bit offset:
+  // at most 63 rows of H * D <= 2048 elements (a 24-bit product)
+  const uint32_t rstride = (uint32_t)(a.H * G::ROWB);
   const unsigned char* b0 = (const unsigned char*)x0 + ((r0 * a.H + h) * D) * 2;
   const unsigned char* b1 = (const unsigned char*)x1 + ((r0 * a.H + h) * D) * 2;
   #pragma unroll
@@ -143,7 +183,7 @@ __device__ inline void stage_rows(const BwdArgs& a, const void* x0, const void* 
     const int base = (wave * ND + i) * 64;
     const int P = base + lane;
     const int r = P / G::CPR, pc = P % G::CPR;
-    const int64_t off = min(r, last) * rstride + ((pc ^ swz_b<D>(r)) << 4);
+    const uint32_t off = __umul24((uint32_t)min(r, last), rstride) + (uint32_t)((pc ^ swz_b<D>(r)) << 4);
     __builtin_amdgcn_global_load_lds((const void*)(b0 + off), LDS_PTR(void, st.k + base * 16), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)(b1 + off), LDS_PTR(void, st.v + base * 16), 16, 0, 0);
   }
@@ -271,15 +311,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int n_time_eff = has_time ? min(a.n_time, 64) : 1;
   using LB = __attribute__((address_space(3))) unsigned char;
 
-  auto key_time_range = [&](int j0, int64_t& kmin, int64_t& kmax) {
-    const int64_t r0 = q_off + j0;
-    const int64_t i0 = min(r0 / KT, a.n_stat_blocks - 1), i1 = min((r0 + KT - 1) / KT, a.n_stat_blocks - 1);
-    kmin = min(ldc(a.tstats + 2 * i0), ldc(a.tstats + 2 * i1));
-    kmax = max(ldc(a.tstats + 2 * i0 + 1), ldc(a.tstats + 2 * i1 + 1));
-    if (kmin > kmax) kmin = kmax = w_ts_min;
-  };
-
-  auto compute_tile = [&](Stage<T, D>& st, int j0) {
+  int tcls = 0;  // this lane's tile time class (time_class), filled 64 tiles at a time
+  auto compute_tile = [&](Stage<T, D>& st, int j0, int t) {
     if (!w_rows || j0 > w_lim_max) return;
     const bool need_mask = j0 + KT - 1 > w_lim_min;
     // one bias constant for the whole wave tile?
@@ -287,19 +320,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     bool time_uniform = !has_time;
     int z_tile = 63;
     bool small_span = true;
-    if (has_time) {
-      int64_t k_min, k_max;
-      key_time_range(j0, k_min, k_max);
-      const int64_t d1 = w_ts_max - k_min, d2 = k_max - w_ts_min;
-      small_span = max(d1 < 0 ? -d1 : d1, d2 < 0 ? -d2 : d2) < ((int64_t)1 << 31) - 2;
-      int64_t lo = -1, hi = -1;
-      if (w_ts_min >= k_max) { lo = w_ts_min - k_max; hi = w_ts_max - k_min; }
-      else if (k_min >= w_ts_max) { lo = k_min - w_ts_max; hi = k_max - w_ts_min; }
-      if (lo >= 0) {
-        const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
-        if (min(63 - zlo, n_time_eff - 1) == min(63 - zhi, n_time_eff - 1)) { time_uniform = true; z_tile = zlo; }
-      }
-    }
+    if (has_time) tile_class(tcls, t, time_uniform, z_tile, small_span);
     const bool fast = pos_uniform && time_uniform && !need_mask;
     const float c_uni = (a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f) + (has_time ? tab.time_t[z_tile] : 0.0f);
     const int lim_rel = p_lane - j0 - M::HLK * hl;  // key_of(kb, v, 0) <= lim_rel: allowed
@@ -436,14 +457,27 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   } else {
     __syncthreads();
   }
+  // time classes of the next 64 tiles, lane i for tile t0 + i; the loads are
+  // issued before the step's DMA, so waiting for them does not wait for it
+  auto time_batch = [&](int t0) {
+    const int tl = t0 + lane;
+    int c = 255;
+    if (tl < ntiles) {
+      int64_t mn, mx;
+      row_time_range(a, q_off + k_begin + tl * KT, mn, mx);
+      c = time_class(mn, mx, w_ts_min, w_ts_max, n_time_eff);
+    }
+    tcls = c;
+  };
   for (int t = 0; t < ntiles; t += 2) {
+    if (has_time && (t & 63) == 0) time_batch(t);
     const int j0 = k_begin + t * KT;
     if (t + 1 < ntiles) issue(st1, j0 + KT);
-    compute_tile(st0, j0);
+    compute_tile(st0, j0, t);
     if (t + 1 >= ntiles) break;
     finish_stage<D>(st1, tsreg);
     if (t + 2 < ntiles) issue(st0, j0 + 2 * KT);
-    compute_tile(st1, j0 + KT);
+    compute_tile(st1, j0 + KT, t + 1);
     if (t + 2 < ntiles) finish_stage<D>(st0, tsreg);
   }
 
@@ -574,15 +608,8 @@ __global__ __launch_bounds__(DQ8_THREADS, 2) void attn_bwd_dq8_kernel(BwdArgs a)
   using LV = __attribute__((address_space(3))) const bf16x8;
   using LT = __attribute__((address_space(3))) v4i16;
 
-  auto key_time_range = [&](int j0, int64_t& kmin, int64_t& kmax) {
-    const int64_t r0 = q_off + j0;
-    const int64_t i0 = min(r0 / KT, a.n_stat_blocks - 1), i1 = min((r0 + KT - 1) / KT, a.n_stat_blocks - 1);
-    kmin = min(ldc(a.tstats + 2 * i0), ldc(a.tstats + 2 * i1));
-    kmax = max(ldc(a.tstats + 2 * i0 + 1), ldc(a.tstats + 2 * i1 + 1));
-    if (kmin > kmax) kmin = kmax = w_ts_min;
-  };
-
-  auto compute_tile = [&](Stage<T, D>& st, int j0) {
+  int tcls = 0;  // this lane's tile time class (time_class), filled 64 tiles at a time
+  auto compute_tile = [&](Stage<T, D>& st, int j0, int t) {
     const int jh = j0 + 32 * kh;  // first key of this half
     if (!w_rows || jh > w_lim_max) return;
     const bool need_mask = jh + 31 > w_lim_min;
@@ -591,19 +618,7 @@ __global__ __launch_bounds__(DQ8_THREADS, 2) void attn_bwd_dq8_kernel(BwdArgs a)
     bool time_uniform = !has_time;
     int z_tile = 63;
     bool small_span = true;
-    if (has_time) {
-      int64_t k_min, k_max;
-      key_time_range(j0, k_min, k_max);
-      const int64_t d1 = w_ts_max - k_min, d2 = k_max - w_ts_min;
-      small_span = max(d1 < 0 ? -d1 : d1, d2 < 0 ? -d2 : d2) < ((int64_t)1 << 31) - 2;
-      int64_t lo = -1, hi = -1;
-      if (w_ts_min >= k_max) { lo = w_ts_min - k_max; hi = w_ts_max - k_min; }
-      else if (k_min >= w_ts_max) { lo = k_min - w_ts_max; hi = k_max - w_ts_min; }
-      if (lo >= 0) {
-        const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
-        if (min(63 - zlo, n_time_eff - 1) == min(63 - zhi, n_time_eff - 1)) { time_uniform = true; z_tile = zlo; }
-      }
-    }
+    if (has_time) tile_class(tcls, t, time_uniform, z_tile, small_span);
     const bool fast = pos_uniform && time_uniform && !need_mask;
     const float c_uni = (a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f) + (has_time ? tab.time_t[z_tile] : 0.0f);
     const int lim_rel = p_lane - j0 - M::HLK * hl;  // key_of(kh, v, 0) <= lim_rel: allowed
@@ -737,14 +752,27 @@ __global__ __launch_bounds__(DQ8_THREADS, 2) void attn_bwd_dq8_kernel(BwdArgs a)
   } else {
     __syncthreads();
   }
+  // time classes of the next 64 tiles, lane i for tile t0 + i; the loads are
+  // issued before the step's DMA, so waiting for them does not wait for it
+  auto time_batch = [&](int t0) {
+    const int tl = t0 + lane;
+    int c = 255;
+    if (tl < ntiles) {
+      int64_t mn, mx;
+      row_time_range(a, q_off + k_begin + tl * KT, mn, mx);
+      c = time_class(mn, mx, w_ts_min, w_ts_max, n_time_eff);
+    }
+    tcls = c;
+  };
   for (int t = 0; t < ntiles; t += 2) {
+    if (has_time && (t & 63) == 0) time_batch(t);
     const int j0 = k_begin + t * KT;
     if (t + 1 < ntiles) issue(st1, j0 + KT);
-    compute_tile(st0, j0);
+    compute_tile(st0, j0, t);
     if (t + 1 >= ntiles) break;
     finish_stage<D>(st1, tsreg);
     if (t + 2 < ntiles) issue(st0, j0 + 2 * KT);
-    compute_tile(st1, j0 + KT);
+    compute_tile(st1, j0 + KT, t + 1);
     if (t + 2 < ntiles) finish_stage<D>(st0, tsreg);
   }
 
@@ -903,7 +931,8 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
   const bool has_time = a.time_tab != nullptr;
   using LB = __attribute__((address_space(3))) unsigned char;
 
-  auto compute_tile = [&](Stage<T, D>& st, int j0) {
+  int tcls = 0;  // this lane's tile time class (time_class), filled 64 tiles at a time
+  auto compute_tile = [&](Stage<T, D>& st, int j0, int t) {
     // every query of the tile precedes every key of this wave: all masked
     if (!w_keys || j0 + KT - 1 < w_kmin) return;
     // one bias constant and no mask for the whole wave tile? (as in the forward)
@@ -912,23 +941,7 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
     bool time_uniform = !has_time;
     int z_tile = 63;
     bool small_span = true;
-    if (has_time) {
-      const int64_t r0 = q_off + j0;
-      const int64_t i0 = min(r0 / KT, a.n_stat_blocks - 1), i1 = min((r0 + KT - 1) / KT, a.n_stat_blocks - 1);
-      int64_t q_min = min(ldc(a.tstats + 2 * i0), ldc(a.tstats + 2 * i1));
-      int64_t q_max = max(ldc(a.tstats + 2 * i0 + 1), ldc(a.tstats + 2 * i1 + 1));
-      if (q_min > q_max) q_min = q_max = w_ts_min;
-      // rows past the user's end (last tile) are clamped copies of its last row
-      const int64_t d1 = q_max - w_ts_min, d2 = w_ts_max - q_min;
-      small_span = max(d1 < 0 ? -d1 : d1, d2 < 0 ? -d2 : d2) < ((int64_t)1 << 31) - 2;
-      int64_t lo = -1, hi = -1;
-      if (q_min >= w_ts_max) { lo = q_min - w_ts_max; hi = q_max - w_ts_min; }
-      else if (w_ts_min >= q_max) { lo = w_ts_min - q_max; hi = w_ts_max - q_min; }
-      if (lo >= 0 && !need_mask && pos_uniform) {
-        const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
-        if (min(63 - zlo, n_time_eff - 1) == min(63 - zhi, n_time_eff - 1)) { time_uniform = true; z_tile = zlo; }
-      }
-    }
+    if (has_time) tile_class(tcls, t, time_uniform, z_tile, small_span);
     const bool fast = pos_uniform && time_uniform && !need_mask;
     const float c_uni = (a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f) + (has_time ? tab.time_t[z_tile] : 0.0f);
     const int64_t* ts_l = st.ts64 + M::HLK * hl;
@@ -1035,14 +1048,27 @@ __global__ __launch_bounds__(NTHREADS, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
   };
   issue(st0, k0);
   finish_stage<D>(st0, tsreg);
+  // time classes of the next 64 tiles, lane i for tile t0 + i; the loads are
+  // issued before the step's DMA, so waiting for them does not wait for it
+  auto time_batch = [&](int t0) {
+    const int tl = t0 + lane;
+    int c = 255;
+    if (tl < ntiles) {
+      int64_t mn, mx;
+      row_time_range(a, q_off + k0 + tl * KT, mn, mx);
+      c = time_class(mn, mx, w_ts_min, w_ts_max, n_time_eff);
+    }
+    tcls = c;
+  };
   for (int t = 0; t < ntiles; t += 2) {
+    if (has_time && (t & 63) == 0) time_batch(t);
     const int j0 = k0 + t * KT;
     if (t + 1 < ntiles) issue(st1, j0 + KT);
-    compute_tile(st0, j0);
+    compute_tile(st0, j0, t);
     if (t + 1 >= ntiles) break;
     finish_stage<D>(st1, tsreg);
     if (t + 2 < ntiles) issue(st0, j0 + 2 * KT);
-    compute_tile(st1, j0 + KT);
+    compute_tile(st1, j0 + KT, t + 1);
     if (t + 2 < ntiles) finish_stage<D>(st0, tsreg);
   }
   store_rows_t<D>(dvacc, -LN2 / (float)n_norm, st0, st1, a.dv, q_off + k0, klen, h, H);
@@ -1165,7 +1191,8 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
   LB* kl = LDS_PTR(unsigned char, kv.k);
   LB* vl = LDS_PTR(unsigned char, kv.v);
 
-  auto compute_tile = [&](Stage<T, D>& st, int j0) {
+  int tcls = 0;  // this lane's tile time class (time_class), filled 64 tiles at a time
+  auto compute_tile = [&](Stage<T, D>& st, int j0, int t) {
     // every query of this half precedes every key of this wave: all masked
     if (!w_keys || j0 + 32 * qb + 31 < w_kmin) return;
     // one bias constant and no mask for the whole wave tile? (as in the forward)
@@ -1174,23 +1201,7 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
     bool time_uniform = !has_time;
     int z_tile = 63;
     bool small_span = true;
-    if (has_time) {
-      const int64_t r0 = q_off + j0;
-      const int64_t i0 = min(r0 / KT, a.n_stat_blocks - 1), i1 = min((r0 + KT - 1) / KT, a.n_stat_blocks - 1);
-      int64_t q_min = min(ldc(a.tstats + 2 * i0), ldc(a.tstats + 2 * i1));
-      int64_t q_max = max(ldc(a.tstats + 2 * i0 + 1), ldc(a.tstats + 2 * i1 + 1));
-      if (q_min > q_max) q_min = q_max = w_ts_min;
-      // rows past the user's end (last tile) are clamped copies of its last row
-      const int64_t d1 = q_max - w_ts_min, d2 = w_ts_max - q_min;
-      small_span = max(d1 < 0 ? -d1 : d1, d2 < 0 ? -d2 : d2) < ((int64_t)1 << 31) - 2;
-      int64_t lo = -1, hi = -1;
-      if (q_min >= w_ts_max) { lo = q_min - w_ts_max; hi = q_max - w_ts_min; }
-      else if (w_ts_min >= q_max) { lo = w_ts_min - q_max; hi = w_ts_max - q_min; }
-      if (lo >= 0 && !need_mask && pos_uniform) {
-        const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
-        if (min(63 - zlo, n_time_eff - 1) == min(63 - zhi, n_time_eff - 1)) { time_uniform = true; z_tile = zlo; }
-      }
-    }
+    if (has_time) tile_class(tcls, t, time_uniform, z_tile, small_span);
     const bool fast = pos_uniform && time_uniform && !need_mask;
     const float c_uni = (a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f) + (has_time ? tab.time_t[z_tile] : 0.0f);
     const int64_t* ts_l = st.ts64 + M::HLK * hl;
@@ -1303,14 +1314,27 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
   };
   issue(st0, k0);
   finish_stage<D>(st0, tsreg);  // also waits for the K and V rows
+  // time classes of the next 64 tiles, lane i for tile t0 + i; the loads are
+  // issued before the step's DMA, so waiting for them does not wait for it
+  auto time_batch = [&](int t0) {
+    const int tl = t0 + lane;
+    int c = 255;
+    if (tl < ntiles) {
+      int64_t mn, mx;
+      row_time_range(a, q_off + k0 + tl * KT, mn, mx);
+      c = time_class(mn, mx, w_ts_min, w_ts_max, n_time_eff);
+    }
+    tcls = c;
+  };
   for (int t = 0; t < ntiles; t += 2) {
+    if (has_time && (t & 63) == 0) time_batch(t);
     const int j0 = k0 + t * KT;
     if (t + 1 < ntiles) issue(st1, j0 + KT);
-    compute_tile(st0, j0);
+    compute_tile(st0, j0, t);
     if (t + 1 >= ntiles) break;
     finish_stage<D>(st1, tsreg);
     if (t + 2 < ntiles) issue(st0, j0 + 2 * KT);
-    compute_tile(st1, j0 + KT);
+    compute_tile(st1, j0 + KT, t + 1);
     if (t + 2 < ntiles) finish_stage<D>(st0, tsreg);
   }
 
