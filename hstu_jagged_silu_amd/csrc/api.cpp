@@ -118,7 +118,8 @@ bool layout(int fn, const hstu_params_t* p, int32_t B, int64_t Tq, int64_t max_l
   w.stats_off = align_up(w.scratch_off + (size_t)(B + 1) * sizeof(int32_t));
   w.o_off = align_up(w.stats_off + (size_t)w.n_stat_blocks * 2 * sizeof(int64_t));
   w.total = align_up(w.o_off + (size_t)w.n_chunks * (size_t)Tq * (size_t)HD * sizeof(float));
-  w.dout_off = w.rab_off = w.lnp_off = w.total;
+  w.dout_off = w.rab_off = w.lnp_off = w.ds_off = w.dsp_off = w.total;
+  w.ds_blocks = 0;
   w.ln_waves = 0;
   if (fn == HSTU_FN_FULL_BWD) {
     const bool tables = p->pos_tab || p->time_tab;
@@ -127,6 +128,16 @@ bool layout(int fn, const hstu_params_t* p, int32_t B, int64_t Tq, int64_t max_l
     w.rab_off = align_up(w.dout_off + (size_t)Tq * (size_t)HD * 2);
     w.lnp_off = align_up(w.rab_off + (tables ? (size_t)w.max_items * RAB_SLOTS * sizeof(float) : 0));
     w.total = align_up(w.lnp_off + (affine ? (size_t)2 * w.ln_waves * (size_t)HD * sizeof(float) : 0));
+    w.ds_off = w.dsp_off = w.total;
+    if (p->head_dim == 128) {
+      // dS blocks of 64 x 64: sum_b nb (nb + 1) / 2 <= (n_max + 1) / 2 * sum_b nb,
+      // with nb = ceil(L_b / 64) <= L_b / 64 + 1 and n_max = ceil(max_len / 64)
+      const int64_t nb_sum = ceil_div(Tq, KT) + B, n_max = ceil_div(max_len, KT);
+      if ((double)H * (double)nb_sum * (double)(n_max + 1) > 1e15) return false;
+      w.ds_blocks = H * ceil_div(nb_sum * (n_max + 1), 2);
+      w.ds_off = align_up(w.dsp_off + (size_t)(B + 1) * sizeof(int64_t));
+      w.total = align_up(w.ds_off + (size_t)w.ds_blocks * KT * KT * 2);
+    }
   }
   return true;
 }
@@ -350,6 +361,7 @@ hstu_status_t hstu_attn_bwd(const hstu_params_t* params, int32_t batch, const in
   SchedArgs s = sched_args(MODE_FULL, params, w, ws, batch, seq_offsets, max_len);
   s.ts = ts;
   s.Tk = total_tokens;
+  if (w.ds_blocks > 0) s.ds_prefix = (int64_t*)((char*)ws + w.dsp_off);
   AttnArgs a = base_args(params, w, ws, total_tokens);
   a.q = q;
   a.k = k;
@@ -411,8 +423,13 @@ hstu_status_t hstu_attn_bwd(const hstu_params_t* params, int32_t batch, const in
   g.dk = grads->dk;
   g.dv = grads->dv;
   g.rab_part = (float*)((char*)ws + w.rab_off);
+  if (w.ds_blocks > 0) {
+    g.ds = (bf16*)((char*)ws + w.ds_off);
+    g.ds_prefix = s.ds_prefix;
+    g.ds_cap = w.ds_blocks;
+  }
   if (!mark(2)) return HSTU_ERR_LAUNCH;
-  if (!empty && launch_attn_bwd(g, params->head_dim, s.max_items, max_len, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
+  if (!empty && launch_attn_bwd(g, params->head_dim, s.max_items, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
   // 4. bias-table gradients
   RabReduceArgs r = {};
   r.part = g.rab_part;

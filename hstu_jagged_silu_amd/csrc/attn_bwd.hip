@@ -14,17 +14,20 @@
 // constant factors (-ln2 / N, alpha / N, 1 / N) are applied once, at the end.
 //
 // Two kernels, neither with atomics on global memory:
-//   * attn_bwd_dq_kernel owns 128 query rows (one work item of the forward
-//     scheduler) and walks their key tiles like the forward: S^T = K Q^T and
-//     dP^T = V dO^T on MFMA (K and V rows from LDS, Q and dO in registers),
-//     dS^T elementwise, dQ^T += K^T dS^T (K^T by transposing LDS reads). It
-//     also sums dS into per-wave position/time histograms in LDS.
 //   * attn_bwd_dkdv_kernel owns 128 keys and walks the query tiles that can
 //     see them: S = Q K^T and dP = dO V^T (Q and dO rows from LDS, K and V in
 //     registers), then dV^T += dO^T P and dK^T += Q^T dS. The item of query
 //     tile t of a user maps to key block (tiles - 1 - t), whose cost matches.
 //     For d = 128, attn_bwd_dkdv8_kernel does the same work with eight waves
-//     (two per SIMD) and K and V held in LDS instead of registers.
+//     (two per SIMD) and K and V held in LDS instead of registers, and also
+//     writes dS (bf16) of every causal 64 x 64 block to HBM.
+//   * attn_bwd_dq_kernel owns 128 query rows (one work item of the forward
+//     scheduler) and walks their key tiles like the forward: S^T = K Q^T and
+//     dP^T = V dO^T on MFMA (K and V rows from LDS, Q and dO in registers),
+//     dS^T elementwise, dQ^T += K^T dS^T (K^T by transposing LDS reads). It
+//     also sums dS into per-wave position/time histograms in LDS. For d =
+//     128, attn_bwd_dq_ds_kernel reads the stored dS instead of recomputing
+//     it (dQ^T += K^T dS^T only), after the dK/dV kernel.
 // A third kernel adds the per-item histograms in canonical item order.
 #include <algorithm>
 #include <cmath>
@@ -78,6 +81,11 @@ __device__ inline void row_time_range(const BwdArgs& a, int64_t r0, int64_t& mn,
   mx = max(a.tstats[2 * i0 + 1], a.tstats[2 * i1 + 1]);
 }
 
+__device__ inline int64_t readlane64(int64_t x, int l) {
+  return (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l) |
+         ((int64_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), l) << 32);
+}
+
 // Unpacks a tile's time class (see time_class) for the wave-uniform tile t.
 __device__ inline void tile_class(int tcls, int t, bool& time_uniform, int& z_tile, bool& small_span) {
   const int c = __builtin_amdgcn_readlane(tcls, t & 63);
@@ -101,6 +109,40 @@ __device__ inline void lds_add_f32(float* p, float v) {
   const uint32_t addr = (uint32_t)(uintptr_t)LDS_PTR(float, p);
   asm volatile("ds_add_f32 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
+// The same add without the memory clobber, for a histogram that receives
+// only these adds between two barriers: later LDS reads of other data may
+// then be issued ahead of it instead of waiting for it. The compiler does
+// not count the add in flight, which only makes its own LDS waits stricter
+// (a wave's LDS operations complete in order); the barriers order the adds
+// against the plain accesses before and after.
+__device__ inline void lds_add_f32_unordered(float* p, float v) {
+  const uint32_t addr = (uint32_t)(uintptr_t)LDS_PTR(float, p);
+  asm volatile("ds_add_f32 %0, %1" : : "v"(addr), "v"(v));
+}
+
+// Eight LDS reads (byte addresses in LDS, 16-bit zero-extended or 32-bit),
+// waited for inside the same asm block. For reads of a stage that is
+// complete while a DMA fills the other stage: an ordinary LDS load that the
+// compiler cannot attribute to one stage makes it wait for every DMA in
+// flight first. The early-clobber outputs keep a result from overwriting an
+// address still to be read.
+__device__ inline void lds_read8_u16(const uint32_t (&a)[8], uint32_t (&v)[8]) {
+  asm volatile(
+      "ds_read_u16 %0, %8\n\tds_read_u16 %1, %9\n\tds_read_u16 %2, %10\n\tds_read_u16 %3, %11\n\t"
+      "ds_read_u16 %4, %12\n\tds_read_u16 %5, %13\n\tds_read_u16 %6, %14\n\tds_read_u16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+}
+__device__ inline void lds_read8_b32(const uint32_t (&a)[8], uint32_t (&v)[8]) {
+  asm volatile(
+      "ds_read_b32 %0, %8\n\tds_read_b32 %1, %9\n\tds_read_b32 %2, %10\n\tds_read_b32 %3, %11\n\t"
+      "ds_read_b32 %4, %12\n\tds_read_b32 %5, %13\n\tds_read_b32 %6, %14\n\tds_read_b32 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+}
+__device__ inline float bf16_bits_to_f32(uint32_t x) { return __uint_as_float(x << 16); }
 
 // One histogram per wave (no two waves add to the same word, so every sum
 // runs in program order and the result does not depend on wave timing).
@@ -507,352 +549,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ============================================================================
-// dQ and the bias-table gradients for d = 128: eight waves, two per SIMD
-// ============================================================================
-// Wave w owns the 32 rows of group w mod 4 against the key half w / 4 (32
-// keys) of every 64-key tile, with Q and dO of its rows in registers as in
-// the four-wave kernel; a wave's tile is half as long, so an item's chain of
-// tiles takes about half the time. The two halves' partial dQ sums are added
-// through LDS at the end, half 0 first; each wave keeps its own histograms,
-// added in wave order, so the result does not depend on wave timing.
-constexpr int DQ8_WAVES = 8;
-constexpr int DQ8_THREADS = 64 * DQ8_WAVES;
-// the end of the kernel reuses the two stages: the fp32 partial dQ of half 1
-// (2 row groups x 64 lanes x 64 floats per stage), then the fp32 dQ rows on
-// their way out (64 x 128 per stage)
-static_assert(sizeof(Stage<bf16, 128>) >= QT / 2 * 128 * 4, "reduction buffers");
-
-struct RabHist8 {
-  float pos[DQ8_WAVES][BWD_MAX_NPOS];
-  float time[DQ8_WAVES][64];
-};
-
-__global__ __launch_bounds__(DQ8_THREADS, 2) void attn_bwd_dq8_kernel(BwdArgs a) {
-  constexpr int D = 128;
-  using T = bf16;
-  using G = Geo<T, D>;
-  using M = Mfma<T>;
-  static_assert(G::ROWB == 256 && G::CPR == 16, "resident rows of 256 bytes");
-  __shared__ Stage<T, D> st0;  // k: K rows, v: V rows (both with swz_b)
-  __shared__ Stage<T, D> st1;
-  __shared__ BwdTables tab;
-  __shared__ RabHist8 hist;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qg = wave & 3, kh = wave >> 2;  // row group, key half
-  const int32_t count = ldc(a.count);
-  const WorkItem it = ldc(a.items + blockIdx.x);  // in bounds for every workgroup of the grid
-  if ((int64_t)blockIdx.x >= (int64_t)count) return;
-  const int b = it.b, h = it.h, q_start = it.q_start, q_len = it.q_len;
-  const int k_begin = it.k_begin, k_end = it.k_end;
-  const int H = a.H;
-  const int64_t q_off = it.off;
-  const int L = it.L;
-  const int n_norm = a.norm_n > 0 ? a.norm_n : L;
-  const int n_pos = a.pos_tab ? a.n_pos : 1;
-  load_bwd_tables<DQ8_THREADS>(a, h, tab, n_pos);
-  for (int i = tid; i < DQ8_WAVES * BWD_MAX_NPOS; i += DQ8_THREADS) (&hist.pos[0][0])[i] = 0.0f;
-  for (int i = tid; i < DQ8_WAVES * 64; i += DQ8_THREADS) (&hist.time[0][0])[i] = 0.0f;
-
-  const int row_w = qg * 32 + l32;
-  const bool row_ok = row_w < q_len;
-  const int row_c = min(row_w, q_len - 1);
-  const int64_t qrow = q_off + q_start + row_c;
-  const int p_lane = q_start + row_c;
-  const int64_t tsq = a.ts[qrow];
-  const int w_first = qg * 32;
-  const bool w_rows = w_first < q_len;
-  const int w_last = min(w_first + 31, q_len - 1);
-  const int w_lim_min = q_start + w_first, w_lim_max = q_start + w_last;
-  int64_t w_ts_min = row_ok ? tsq : INT64_MAX, w_ts_max = row_ok ? tsq : INT64_MIN;
-  for (int m = 32; m >= 1; m >>= 1) {
-    w_ts_min = min(w_ts_min, shfl_xor64(w_ts_min, m));
-    w_ts_max = max(w_ts_max, shfl_xor64(w_ts_max, m));
-  }
-  w_ts_min = uniform64(w_ts_min);
-  w_ts_max = uniform64(w_ts_max);
-
-  // Q and dO rows of this lane as MFMA B operands (zero past the item's end,
-  // so those rows' dP, and with it their dS', is zero)
-  bf16x8 qop[G::NQOP], dop[G::NQOP];
-  {
-    const T* qp = (const T*)a.q + (qrow * H + h) * D;
-    const T* gp = (const T*)a.dout + (qrow * H + h) * D;
-    #pragma unroll
-    for (int i = 0; i < G::NQOP; ++i) {
-      bf16x8 x = *(const bf16x8*)(qp + 16 * i + 8 * hl);
-      bf16x8 y = *(const bf16x8*)(gp + 16 * i + 8 * hl);
-      if (!row_ok) { x = bf16x8{}; y = bf16x8{}; }
-      qop[i] = x;
-      dop[i] = y;
-    }
-  }
-
-  // Operand offsets (the chunk of step i of row r sits at (r * 256 + (hl xor
-  // swz(r)) * 16) xor 32i): K / V rows of this key half (A operand, rows in
-  // the order of M::krow), and the transposing K reads of d block db (the
-  // offset of block 0 xor 64db).
-  const int kr = M::krow(0, l32) + 32 * kh;
-  const uint32_t k_base = (uint32_t)(kr * G::ROWB + ((hl ^ swz_b<D>(kr)) << 4));
-  const uint32_t t_base0 = tr_off_b<D>(lane, 0, 0, 0) + kh * 32 * G::ROWB;
-  const uint32_t t_base1 = tr_off_b<D>(lane, 0, 0, 1) + kh * 32 * G::ROWB;
-  f32x16 dqacc[G::NDB];
-  #pragma unroll
-  for (int i = 0; i < G::NDB; ++i) dqacc[i] = f32x16{};
-  const float sc = a.alpha * -LOG2E;
-  const bool has_time = a.time_tab != nullptr;
-  const int n_time_eff = has_time ? min(a.n_time, 64) : 1;
-  using LB = __attribute__((address_space(3))) unsigned char;
-  using LV = __attribute__((address_space(3))) const bf16x8;
-  using LT = __attribute__((address_space(3))) v4i16;
-
-  int tcls = 0;  // this lane's tile time class (time_class), filled 64 tiles at a time
-  auto compute_tile = [&](Stage<T, D>& st, int j0, int t) {
-    const int jh = j0 + 32 * kh;  // first key of this half
-    if (!w_rows || jh > w_lim_max) return;
-    const bool need_mask = jh + 31 > w_lim_min;
-    // one bias constant for the whole wave tile?
-    const bool pos_uniform = (a.pos_tab == nullptr) || (w_lim_min - (jh + 31) >= n_pos - 1);
-    bool time_uniform = !has_time;
-    int z_tile = 63;
-    bool small_span = true;
-    if (has_time) tile_class(tcls, t, time_uniform, z_tile, small_span);
-    const bool fast = pos_uniform && time_uniform && !need_mask;
-    const float c_uni = (a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f) + (has_time ? tab.time_t[z_tile] : 0.0f);
-    const int lim_rel = p_lane - j0 - M::HLK * hl;  // key_of(kh, v, 0) <= lim_rel: allowed
-    const int64_t* ts_l = st.ts64 + M::HLK * hl;
-    const int32_t* tsl_lo = st.ts_lo + M::HLK * hl;
-    const int32_t tsq_lo = (int32_t)tsq;
-    LB* kl = LDS_PTR(unsigned char, st.k);
-    LB* vl = LDS_PTR(unsigned char, st.v);
-    // the bases pass through an empty asm so that the offsets derived from
-    // them are formed here, in every tile, instead of being kept in registers
-    uint32_t kb_t = k_base, tb0 = t_base0, tb1 = t_base1;
-    asm volatile("" : "+v"(kb_t), "+v"(tb0), "+v"(tb1));
-
-    // S^T = K Q^T and dP^T = V dO^T as two interleaved chains, the K and V
-    // operands of step i + 1 read while the MFMAs of step i run
-    f32x16 s = f32x16{}, dp = f32x16{};
-    bf16x8 op[2][2];
-    auto read_step = [&](int i, bf16x8* o) {
-      const uint32_t ko = kb_t ^ (uint32_t)(i << 5);
-      o[0] = *(LV*)(kl + ko);
-      o[1] = *(LV*)(vl + ko);
-    };
-    read_step(0, op[0]);
-    #pragma unroll
-    for (int i = 0; i < G::NQOP; ++i) {
-      if (i + 1 < G::NQOP) read_step(i + 1, op[(i + 1) & 1]);
-      s = M::run(op[i & 1][0], qop[i], s);
-      dp = M::run(op[i & 1][1], dop[i], dp);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    bf16x8 dsb[2];
-    if (fast) {
-      float tile_sum = 0.0f;
-      #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float p, ds;
-        silu_fwd_bwd(fmaf(s[v], sc, c_uni), dp[v], p, ds);
-        tile_sum += ds;
-        dsb[v >> 3][v & 7] = (bf16)ds;
-      }
-      // rows past q_len have zero dO, so their dS' is 0 and they add nothing
-      const float tot = wave_sum_f(tile_sum);
-      if (lane == 0) {
-        if (a.pos_tab) hist.pos[wave][n_pos - 1] += tot;
-        if (has_time) hist.time[wave][min(63 - z_tile, n_time_eff - 1)] += tot;
-      }
-    } else {
-      // a lane's keys come in increasing order along v, so with ordered
-      // timestamps its time bucket (and a clamped position bucket) stays the
-      // same over runs of keys: dS' is summed per run and added to the
-      // wave's histogram when the bucket changes, not once per pair
-      int cur_p = -1, cur_t = -1;
-      float run_p = 0.0f, run_t = 0.0f;
-      auto general = [&](auto small_tag) {
-        constexpr bool SMALL = decltype(small_tag)::value;
-        #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kk = M::key_of(kh, v, 0);
-          const bool ok = kk <= lim_rel;
-          const int rel = lim_rel - kk;  // query position - key position
-          const int pb = min((unsigned)rel, (unsigned)(n_pos - 1));
-          float cb = a.pos_tab ? tab.pos_t[pb] : 0.0f;
-          int tb = 0;
-          if (has_time) {
-            const int zc = time_z<SMALL>(tsq, SMALL ? 0 : ts_l[kk], tsq_lo, SMALL ? tsl_lo[kk] : 0);
-            cb += tab.time_t[zc];
-            tb = min(63 - zc, n_time_eff - 1);
-          }
-          float p, ds;
-          silu_fwd_bwd(ok ? fmaf(s[v], sc, cb) : MASKED_Y, dp[v], p, ds);
-          dsb[v >> 3][v & 7] = (bf16)ds;
-          if (ok && row_ok) {
-            if (a.pos_tab) {
-              if (pb != cur_p) {
-                if (cur_p >= 0) lds_add_f32(&hist.pos[wave][cur_p], run_p);
-                cur_p = pb;
-                run_p = 0.0f;
-              }
-              run_p += ds;
-            }
-            if (has_time) {
-              if (tb != cur_t) {
-                if (cur_t >= 0) lds_add_f32(&hist.time[wave][cur_t], run_t);
-                cur_t = tb;
-                run_t = 0.0f;
-              }
-              run_t += ds;
-            }
-          }
-        }
-      };
-      if (small_span) general(std::true_type{});
-      else general(std::false_type{});
-      if (cur_p >= 0) lds_add_f32(&hist.pos[wave][cur_p], run_p);
-      if (cur_t >= 0) lds_add_f32(&hist.time[wave][cur_t], run_t);
-    }
-
-    // dQ^T += K^T dS^T for the 32 keys of this half, the transposed operands
-    // of d block db + 1 read during the MFMAs of block db
-    bf16x8 kt[2][2];
-    auto read_tr = [&](int db, bf16x8* o) {
-      #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const uint32_t o0 = (tb0 ^ (uint32_t)(db << 6)) + cc * 16 * G::ROWB;
-        const uint32_t o1 = (tb1 ^ (uint32_t)(db << 6)) + cc * 16 * G::ROWB;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(kl + o0));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)(kl + o1));
-        o[cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    };
-    read_tr(0, kt[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-    for (int db = 0; db < G::NDB; ++db) {
-      if (db + 1 < G::NDB) read_tr(db + 1, kt[(db + 1) & 1]);
-      #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) dqacc[db] = M::run(kt[db & 1][cc], dsb[cc], dqacc[db]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  const int ntiles = k_end > k_begin ? (int)ceil_div(k_end - k_begin, KT) : 0;
-  int64_t tsreg = 0;
-  auto issue = [&](Stage<T, D>& st, int j0) {
-    stage_rows<D, DQ8_WAVES>(a, a.k, a.v, st, q_off + j0, min(KT, L - j0), h, tsreg);
-  };
-  if (ntiles > 0) {
-    issue(st0, k_begin);
-    finish_stage<D>(st0, tsreg);  // also orders the tables and histograms
-  } else {
-    __syncthreads();
-  }
-  // time classes of the next 64 tiles, lane i for tile t0 + i; the loads are
-  // issued before the step's DMA, so waiting for them does not wait for it
-  auto time_batch = [&](int t0) {
-    const int tl = t0 + lane;
-    int c = 255;
-    if (tl < ntiles) {
-      int64_t mn, mx;
-      row_time_range(a, q_off + k_begin + tl * KT, mn, mx);
-      c = time_class(mn, mx, w_ts_min, w_ts_max, n_time_eff);
-    }
-    tcls = c;
-  };
-  for (int t = 0; t < ntiles; t += 2) {
-    if (has_time && (t & 63) == 0) time_batch(t);
-    const int j0 = k_begin + t * KT;
-    if (t + 1 < ntiles) issue(st1, j0 + KT);
-    compute_tile(st0, j0, t);
-    if (t + 1 >= ntiles) break;
-    finish_stage<D>(st1, tsreg);
-    if (t + 2 < ntiles) issue(st0, j0 + 2 * KT);
-    compute_tile(st1, j0 + KT, t + 1);
-    if (t + 2 < ntiles) finish_stage<D>(st0, tsreg);
-  }
-
-  // half 1 hands its partial dQ to half 0 ([group][db][4][lane] x f32x4,
-  // groups 0, 1 in stage 0 and 2, 3 in stage 1), then the fp32 rows go out as
-  // bf16 through the same space
-  __syncthreads();
-  using LF4 = __attribute__((address_space(3))) f32x4;
-  LF4* red = LDS_PTR(f32x4, qg < 2 ? (void*)&st0 : (void*)&st1) + (qg & 1) * (G::NDB * 4 * 64) + lane;
-  if (kh == 1) {
-    #pragma unroll
-    for (int db = 0; db < G::NDB; ++db) {
-      #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        red[(db * 4 + g) * 64] = f32x4{dqacc[db][4 * g], dqacc[db][4 * g + 1], dqacc[db][4 * g + 2], dqacc[db][4 * g + 3]};
-    }
-  }
-  __syncthreads();
-  if (kh == 0) {
-    #pragma unroll
-    for (int db = 0; db < G::NDB; ++db) {
-      #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 x = red[(db * 4 + g) * 64];
-        #pragma unroll
-        for (int j = 0; j < 4; ++j) dqacc[db][4 * g + j] += x[j];
-      }
-    }
-  }
-  __syncthreads();
-  // fp32 rows 0..63 in stage 0 and 64..127 in stage 1, chunk c of row r at c xor (r mod 32)
-  constexpr int OCPR = D / 4;
-  using LFP = __attribute__((address_space(3))) float;
-  auto orow = [&](int r) -> LFP* { return LDS_PTR(float, r < 64 ? (void*)&st0 : (void*)&st1) + (r & 63) * D; };
-  if (kh == 0) {
-    const float sq = a.alpha / (float)n_norm;
-    #pragma unroll
-    for (int db = 0; db < G::NDB; ++db) {
-      #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = (32 * db + 8 * g + 4 * hl) / 4;
-        *(LF4*)(orow(row_w) + (c ^ (row_w % OCPR)) * 4) =
-            f32x4{dqacc[db][4 * g] * sq, dqacc[db][4 * g + 1] * sq, dqacc[db][4 * g + 2] * sq, dqacc[db][4 * g + 3] * sq};
-      }
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < QT * OCPR; i += DQ8_THREADS) {
-    const int r = i / OCPR, c = i % OCPR;
-    if (r < q_len) {
-      const f32x4 x = *(const LF4*)(orow(r) + (c ^ (r % OCPR)) * 4);
-      const bf16x4 v = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
-      *(bf16x4*)((bf16*)a.dq + ((q_off + q_start + r) * H + h) * D + c * 4) = v;
-    }
-  }
-
-  // per-item bias gradients (scaled by 1 / N), head-major: the items of head h
-  // are [h * tiles, (h + 1) * tiles), tiles = query tiles over all users
-  // (the scheduler's prefix counts H items per tile); waves added in order
-  const int64_t tiles = ldc(a.prefix + a.B) / H;
-  const int64_t canon = (int64_t)h * tiles + ldc(a.prefix + b) / H + q_start / QT;
-  float* part = a.rab_part + canon * RAB_SLOTS;
-  const float inv_n = 1.0f / (float)n_norm;
-  if (a.pos_tab) {
-    for (int i = tid; i < n_pos; i += DQ8_THREADS) {
-      float x = 0.0f;
-      #pragma unroll
-      for (int w = 0; w < DQ8_WAVES; ++w) x += hist.pos[w][i];
-      part[i] = x * inv_n;
-    }
-  }
-  if (has_time && tid < 64) {
-    float x = 0.0f;
-    #pragma unroll
-    for (int w = 0; w < DQ8_WAVES; ++w) x += hist.time[w][tid];
-    part[BWD_MAX_NPOS + tid] = x * inv_n;
-  }
-}
-
-// ============================================================================
 // dK and dV: 128 keys, all query tiles at or after them
 // ============================================================================
 template <int D>
@@ -1132,6 +828,23 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
   const int klen = min(QT, L - k0);
   const int n_pos = a.pos_tab ? a.n_pos : 1;
   load_bwd_tables<DKDV8_THREADS>(a, h, tab, n_pos);
+  // dS of every causal 64 x 64 (key, query) block of the user goes to HBM
+  // for the dQ kernel: this wave writes key rows 32 (kg mod 2) .. + 31 of
+  // block row kt, query columns 32 qb .. + 31 (8 per half-wave and register
+  // group), zeros where the pair is masked
+  const int nbb = (int)ceil_div(L, KT);
+  const int64_t ds_blk0 = (int64_t)H * ldc(a.ds_prefix + it.b) + (int64_t)h * nbb * (nbb + 1) / 2;
+  const int ds_kt = k0 / KT + (kg >> 1);
+  const uint32_t ds_lane = (uint32_t)((32 * (kg & 1) + l32) * KT + 32 * qb + 8 * hl);
+  auto store_ds = [&](int j0, bf16x8 x0, bf16x8 x1) {
+    const int qt = j0 / KT;
+    const int64_t gb = ds_blk0 + (int64_t)qt * (qt + 1) / 2 + ds_kt;
+    if (gb < a.ds_cap) {
+      bf16* p = a.ds + gb * (KT * KT) + ds_lane;
+      __builtin_nontemporal_store(x0, (bf16x8*)p);
+      __builtin_nontemporal_store(x1, (bf16x8*)(p + 16));
+    }
+  };
 
   // K and V of the 128 keys into LDS (rows past the user's end are copies of
   // its last row; their pairs are masked): 2,048 16-byte chunks per tensor
@@ -1193,7 +906,9 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
 
   int tcls = 0;  // this lane's tile time class (time_class), filled 64 tiles at a time
   auto compute_tile = [&](Stage<T, D>& st, int j0, int t) {
-    // every query of this half precedes every key of this wave: all masked
+    // every query of this half precedes every key of this wave (or the
+    // wave has no keys): all masked (the zeros of its dS are written after
+    // the loop)
     if (!w_keys || j0 + 32 * qb + 31 < w_kmin) return;
     // one bias constant and no mask for the whole wave tile? (as in the forward)
     const bool need_mask = !w_full || j0 < w_kmax || j0 + KT > L;
@@ -1277,6 +992,7 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
       if (small_span) general(std::true_type{});
       else general(std::false_type{});
     }
+    store_ds(j0, dsb[0], dsb[1]);
     // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries of this half,
     // the transposed operands of step db + 1 read during the MFMAs of step db
     bf16x8 tp[2][4];
@@ -1336,6 +1052,13 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
     if (t + 2 < ntiles) issue(st0, j0 + 2 * KT);
     compute_tile(st1, j0 + KT, t + 1);
     if (t + 2 < ntiles) finish_stage<D>(st0, tsreg);
+  }
+  // the all-masked wave tiles of existing dS blocks: zeros (a separate loop,
+  // so that the tile loop keeps its register allocation)
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = k0 + t * KT;
+    if ((!w_keys || j0 + 32 * qb + 31 < w_kmin) && ds_kt <= j0 / KT && ds_kt * KT < L)
+      store_ds(j0, bf16x8{}, bf16x8{});
   }
 
   // half 1 hands its partial sums to half 0, per tensor [key group][db][4][lane]
@@ -1408,6 +1131,470 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
 }
 
 // ============================================================================
+// dQ and the bias-table gradients for d = 128 from the stored dS
+// ============================================================================
+// The eight-wave dK/dV kernel has already written dS of every causal 64 x 64
+// (key, query) block to HBM, so no score is recomputed here: for each key
+// tile of a work item (128 query rows) the workgroup stages the K rows and
+// the item's two dS blocks of that tile in LDS, and wave w (rows 32w .. 32w
+// + 31, columns 32 (w mod 2) .. of block w / 2) adds K^T dS^T to its dQ^T
+// (16 MFMAs per tile, both operands from transposing reads). The histograms
+// of the bias-table gradients sum the same bf16 dS values the MFMAs use. The
+// kernel is bound by the dS stream from HBM.
+
+// LDS layout of a dS block: 64 key rows of 64 bf16 queries (128 bytes), the
+// 16-byte chunk c of row r at c xor (2r mod 8). The transposing reads of a
+// B operand cover 4 consecutive rows x 64 bytes per 256-byte window, which
+// this swizzle spreads over 64 distinct banks.
+constexpr int DS_BLOCK = KT * KT;  // elements of one block
+__device__ inline uint32_t ds_chunk_off(int r, int c) { return (uint32_t)(r * (KT * 2) + ((c ^ ((2 * r) & 7)) << 4)); }
+// This lane's transposing read of a dS block: key rows 8 (lane / 32) + 4 s4
+// + 0..3 (plus 16 per key step), query column 32 db + lane mod 32.
+__device__ inline uint32_t ds_tr_off(int lane, int db, int s4) {
+  const int tr_g = lane >> 4, tr_j = lane & 15;
+  const int row = 8 * (tr_g >> 1) + 4 * s4 + (tr_j >> 2);
+  const int col = 32 * db + 16 * (tr_g & 1) + 4 * (tr_j & 3);
+  return ds_chunk_off(row, col >> 3) + (uint32_t)((col & 7) * 2);
+}
+
+__global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_ds_kernel(BwdArgs a) {
+  constexpr int D = 128;
+  using T = bf16;
+  using G = Geo<T, D>;
+  __shared__ Stage<T, D> st0;  // k: K rows (swz_b), v: the item's two dS blocks of the tile
+  __shared__ Stage<T, D> st1;
+  __shared__ RabHist hist;
+  static_assert(sizeof(Stage<T, D>::v) == 2 * DS_BLOCK * 2, "two dS blocks per stage");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t count = ldc(a.count);
+  const WorkItem it = ldc(a.items + blockIdx.x);  // in bounds for every workgroup of the grid
+  if ((int64_t)blockIdx.x >= (int64_t)count) return;
+  const int b = it.b, h = it.h, q_start = it.q_start, q_len = it.q_len;
+  const int k_begin = it.k_begin, k_end = it.k_end;
+  const int H = a.H;
+  const int64_t q_off = it.off;
+  const int L = it.L;
+  const int n_norm = a.norm_n > 0 ? a.norm_n : L;
+  const bool has_pos = a.pos_tab != nullptr, has_time = a.time_tab != nullptr;
+  const int n_pos = has_pos ? a.n_pos : 1;
+  const int n_time_eff = has_time ? min(a.n_time, 64) : 1;
+  if (has_pos)
+    for (int i = tid; i < NWAVES * BWD_MAX_NPOS; i += NTHREADS) (&hist.pos[0][0])[i] = 0.0f;
+  if (has_time)
+    for (int i = tid; i < NWAVES * 64; i += NTHREADS) (&hist.time[0][0])[i] = 0.0f;
+
+  const int row_w = wave * 32 + (lane & 31);
+  const bool row_ok = row_w < q_len;
+  const int p_lane = q_start + min(row_w, q_len - 1);
+  const int64_t tsq = a.ts[q_off + p_lane];
+  const int w_first = wave * 32;
+  const bool w_rows = w_first < q_len;
+  const int w_last = min(w_first + 31, q_len - 1);
+  const int w_lim_min = q_start + w_first, w_lim_max = q_start + w_last;
+  int64_t w_ts_min = row_ok ? tsq : INT64_MAX, w_ts_max = row_ok ? tsq : INT64_MIN;
+  for (int m = 32; m >= 1; m >>= 1) {
+    w_ts_min = min(w_ts_min, shfl_xor64(w_ts_min, m));
+    w_ts_max = max(w_ts_max, shfl_xor64(w_ts_max, m));
+  }
+  w_ts_min = uniform64(w_ts_min);
+  w_ts_max = uniform64(w_ts_max);
+
+  // dS blocks of this user and head; block (kt, qt) at blk0 + qt (qt + 1) / 2 + kt
+  const int nbb = (int)ceil_div(L, KT);
+  const int64_t blk0 = (int64_t)H * ldc(a.ds_prefix + b) + (int64_t)h * nbb * (nbb + 1) / 2;
+  const int qt0 = q_start / KT;
+  const int qt_w = qt0 + (wave >> 1);  // block column of this wave's rows (and of its DMA)
+
+  // K^T operands (A) of d block db and key step ks: the offset of (0, 0) xor
+  // 64 db, plus 16 rows per step; dS^T operands (B) of key step ks
+  const uint32_t t_base0 = tr_off_b<D>(lane, 0, 0, 0), t_base1 = tr_off_b<D>(lane, 0, 0, 1);
+  const uint32_t s_base0 = ds_tr_off(lane, wave & 1, 0) + (uint32_t)((wave >> 1) * DS_BLOCK * 2);
+  const uint32_t s_base1 = ds_tr_off(lane, wave & 1, 1) + (uint32_t)((wave >> 1) * DS_BLOCK * 2);
+  f32x16 dqacc[G::NDB];
+  #pragma unroll
+  for (int i = 0; i < G::NDB; ++i) dqacc[i] = f32x16{};
+  using LB = __attribute__((address_space(3))) unsigned char;
+  using LT = __attribute__((address_space(3))) v4i16;
+  // LDS reads through address-space-3 pointers derived from the stage: the
+  // compiler then sees which stage they read and does not wait for the DMA
+  // that is filling the other one
+  using LH = __attribute__((address_space(3))) const bf16;
+  using LI = __attribute__((address_space(3))) const int32_t;
+  using LL = __attribute__((address_space(3))) const int64_t;
+  using LFP = __attribute__((address_space(3))) float;
+  auto tr8 = [](LB* p0, LB* p1) {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)p0);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LT*)p1);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  int tcls = 0;  // this lane's tile time class (time_class), filled 64 tiles at a time
+  int64_t tb_mn = 0, tb_mx = 0;  // and the timestamp range (a superset) of that tile's keys
+  bf16x8 ones;
+  #pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = (bf16)1.0f;
+  // Histogram state. LDS float atomics are slow, so the sums are kept in
+  // registers and reduced across the wave only rarely: pos_acc (MFMA sums of
+  // the tiles entirely in bucket n_pos - 1) and pos_far (that bucket's pairs
+  // in the other tiles) once per item; time_acc (MFMA sums
+  // of the tiles in time bucket time_cur) folds into a per-lane window of 8
+  // time buckets [wb, wb + 8), reduced when the window moves (time buckets
+  // fall along an item's key tiles when timestamps grow with position).
+  f32x16 pos_acc = f32x16{}, time_acc = f32x16{};
+  float pos_far = 0.0f;  // per lane: its pairs at distance n_pos - 1 or more in the other tiles
+  int time_cur = -1;
+  float win[8];
+  #pragma unroll
+  for (int s = 0; s < 8; ++s) win[s] = 0.0f;
+  int wb = 0;
+  auto flush_win = [&]() {
+    #pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float x = wave_sum_f(win[s]);
+      if (lane == 0 && wb + s < 64) lds_add_f32_unordered(&hist.time[wave][wb + s], x);
+      win[s] = 0.0f;
+    }
+  };
+  // make buckets [lo, hi] (hi - lo < 8, wave-uniform) fit the window
+  auto win_fit = [&](int lo, int hi) {
+    if (lo < wb || hi >= wb + 8) {
+      flush_win();
+      wb = max(0, hi - 7);
+    }
+  };
+  auto win_add = [&](int bkt, float v) {
+    #pragma unroll
+    for (int s = 0; s < 8; ++s) win[s] += bkt - wb == s ? v : 0.0f;
+  };
+  auto fold_time = [&]() {
+    if (time_cur >= 0) {
+      win_fit(time_cur, time_cur);
+      win_add(time_cur, hl == 0 ? time_acc[0] : 0.0f);  // lanes 32..63 repeat lanes 0..31
+      time_acc = f32x16{};
+    }
+  };
+  auto compute_tile = [&](Stage<T, D>& st, int j0, int t) {
+    // keys all after this wave's rows: the block is absent or all zeros
+    if (!w_rows || j0 > w_lim_max) return;
+    LB* kl = LDS_PTR(unsigned char, st.k);
+    LB* dl = LDS_PTR(unsigned char, st.v);
+    uint32_t tb0 = t_base0, tb1 = t_base1, sb0 = s_base0, sb1 = s_base1;
+    asm volatile("" : "+v"(tb0), "+v"(tb1), "+v"(sb0), "+v"(sb1));
+    bf16x8 dsb[4];
+    #pragma unroll
+    for (int ks = 0; ks < 4; ++ks) dsb[ks] = tr8(dl + sb0 + ks * 16 * KT * 2, dl + sb1 + ks * 16 * KT * 2);
+    // dQ^T += K^T dS^T, the K^T operands of step ks + 1 read during the
+    // MFMAs of step ks
+    bf16x8 kt[2][G::NDB];
+    auto read_k = [&](int ks, bf16x8* o) {
+      #pragma unroll
+      for (int db = 0; db < G::NDB; ++db)
+        o[db] = tr8(kl + (tb0 ^ (uint32_t)(db << 6)) + ks * 16 * G::ROWB,
+                    kl + (tb1 ^ (uint32_t)(db << 6)) + ks * 16 * G::ROWB);
+    };
+    read_k(0, kt[0]);
+    #pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks + 1 < 4) read_k(ks + 1, kt[(ks + 1) & 1]);
+      #pragma unroll
+      for (int db = 0; db < G::NDB; ++db) dqacc[db] = Mfma<T>::run(kt[ks & 1][db], dsb[ks], dqacc[db]);
+    }
+    if (!has_pos && !has_time) return;
+    // Bias-table histograms. A sum over a set of pairs is an MFMA of their
+    // dS^T operands against a ones operand (every row of the result holds the
+    // per-query sums; lane l < 32 has query l). Tiles whose pairs all share
+    // the position bucket (n_pos - 1) add into pos_acc, tiles that share one
+    // time bucket into time_acc (flushed when the bucket changes); the other
+    // tiles are handled below
+    const bool pos_uniform = !has_pos || (w_lim_min - (j0 + KT - 1) >= n_pos - 1);
+    bool time_uniform = !has_time;
+    int z_tile = 63;
+    bool small_span = true;
+    if (has_time) tile_class(tcls, t, time_uniform, z_tile, small_span);
+    if (has_pos && pos_uniform) {
+      #pragma unroll
+      for (int ks = 0; ks < 4; ++ks) pos_acc = Mfma<T>::run(ones, dsb[ks], pos_acc);
+    }
+    if (has_time && time_uniform) {
+      const int tb = min(63 - z_tile, n_time_eff - 1);
+      if (tb != time_cur) {
+        fold_time();
+        time_cur = tb;
+      }
+      #pragma unroll
+      for (int ks = 0; ks < 4; ++ks) time_acc = Mfma<T>::run(ones, dsb[ks], time_acc);
+    }
+    if (pos_uniform && time_uniform) return;
+    // the remaining tiles, pair by pair without branches: a masked pair or a
+    // row past the user has dS = 0, so it may be added anywhere in range
+    const int lim_rel = p_lane - j0 - 8 * hl;  // query position - position of tile key 8 hl
+    if (has_pos && !pos_uniform) {
+      // near-diagonal distances r < n_pos - 1: lane r gathers the pairs at
+      // distance r along the wave's valid queries from the dS block in LDS
+      // and adds them to its own bucket (no two lanes share a bucket)
+      LB* blk = dl + (wave >> 1) * DS_BLOCK * 2;
+      const int c0 = (wave & 1) * 32, nq = w_last - w_first + 1;
+      const int r_lo = max(w_lim_min - (j0 + KT - 1), 0), r_hi = min(w_lim_max - j0, n_pos - 2);
+      for (int r0 = r_lo; r0 <= r_hi; r0 += 64) {
+        const int r = r0 + lane;
+        if (r <= r_hi) {
+          float acc = 0.0f;
+          #pragma unroll 1
+          for (int i0 = 0; i0 < 32; i0 += 8) {
+            uint32_t ad[8], v[8];
+            bool ok[8];
+            #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int i = i0 + e, k = w_lim_min + i - r - j0;  // tile key of query i at distance r
+              ok[e] = i < nq && (unsigned)k < (unsigned)KT;
+              const int col = c0 + i;
+              ad[e] = (uint32_t)(uintptr_t)blk + (ok[e] ? ds_chunk_off(k, col >> 3) + (col & 7) * 2 : 0u);
+            }
+            lds_read8_u16(ad, v);
+            #pragma unroll
+            for (int e = 0; e < 8; ++e) acc += ok[e] ? bf16_bits_to_f32(v[e]) : 0.0f;
+          }
+          *(LFP*)&hist.pos[wave][r] += acc;
+        }
+      }
+      // distances n_pos - 1 and beyond: the lane's own pairs, one key step at
+      // a time (a rolled loop keeps the selects from holding many masks)
+      #pragma unroll 1
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 d = ks == 0 ? dsb[0] : ks == 1 ? dsb[1] : ks == 2 ? dsb[2] : dsb[3];
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) pos_far += lim_rel - 16 * ks - j >= n_pos - 1 ? (float)d[j] : 0.0f;
+      }
+    }
+    if (!has_time || time_uniform) return;
+    // Time buckets [b_lo, b_hi] of the wave tile, from the tile's key range
+    // and the wave's query range. When every key precedes every query and
+    // the tile spans at most 4 buckets, a pair is in bucket b_lo + i or above
+    // exactly when t_key <= t_query - (2^(b_lo + i) - 1): one compare per
+    // boundary, summed as nested totals and differenced at the end. Other
+    // tiles (near the diagonal) add pair by pair.
+    const int64_t kmin = readlane64(tb_mn, t & 63), kmax = readlane64(tb_mx, t & 63);
+    int b_lo = 0, nb = 0;
+    if (small_span && kmax <= w_ts_min) {
+      b_lo = min(63 - __builtin_clzll((uint64_t)(w_ts_min - kmax) + 1), n_time_eff - 1);
+      const int b_hi = min(63 - __builtin_clzll((uint64_t)(w_ts_max - kmin) + 1), n_time_eff - 1);
+      nb = b_hi - b_lo + 1;
+    }
+    LI* tsl_lo = LDS_PTR(const int32_t, st.ts_lo) + 8 * hl;
+    const int32_t tsq_lo = (int32_t)tsq;
+    // NB boundaries (NB + 1 buckets from b_lo): per pair, the key's offset
+    // from the query's timestamp against -(2^(b_lo + i + 1) - 1), exact in
+    // 32 bits on a small-span tile
+    auto by_threshold = [&](auto nb_tag) {
+      constexpr int NB = decltype(nb_tag)::value;
+      int32_t bound[NB > 0 ? NB : 1];
+      #pragma unroll
+      for (int i = 0; i < NB; ++i) bound[i] = -(int32_t)(((uint32_t)2 << (b_lo + i)) - 1u);
+      float tot = 0.0f, ge[NB > 0 ? NB : 1] = {};
+      // dS read back from the block in LDS, 8 pairs at a time (holding all
+      // 32 converted values at once would cost registers the kernel lacks)
+      LB* blk = dl + (wave >> 1) * DS_BLOCK * 2;
+      const int col = (wave & 1) * 32 + (lane & 31);
+      #pragma unroll 1
+      for (int ks = 0; ks < 4; ++ks) {
+        uint32_t ad[8], at[8], vd[8], vt[8];
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kk = 16 * ks + 8 * hl + j;
+          ad[j] = (uint32_t)(uintptr_t)blk + ds_chunk_off(kk, col >> 3) + (col & 7) * 2;
+          at[j] = (uint32_t)(uintptr_t)(tsl_lo + 16 * ks + j);
+        }
+        lds_read8_u16(ad, vd);
+        lds_read8_b32(at, vt);
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float ds = bf16_bits_to_f32(vd[j]);
+          const int32_t dk = (int32_t)vt[j] - tsq_lo;
+          tot += ds;
+          #pragma unroll
+          for (int i = 0; i < NB; ++i) ge[i] += dk <= bound[i] ? ds : 0.0f;
+        }
+      }
+      // bucket b_lo + k holds the pairs at or above boundary k - 1 and below boundary k
+      win_fit(b_lo, b_lo + NB);
+      #pragma unroll
+      for (int k = 0; k <= NB; ++k)
+        win_add(b_lo + k, (k == 0 ? tot : ge[k > 0 ? k - 1 : 0]) - (k < NB ? ge[k < NB ? k : 0] : 0.0f));
+    };
+    if (nb == 1) { by_threshold(std::integral_constant<int, 0>{}); return; }
+    if (nb == 2) { by_threshold(std::integral_constant<int, 1>{}); return; }
+    if (nb == 3) { by_threshold(std::integral_constant<int, 2>{}); return; }
+    if (nb == 4) { by_threshold(std::integral_constant<int, 3>{}); return; }
+    // Pair by pair: the window is placed on the tile's highest possible
+    // bucket, so no pair lies above it; pairs below it (only where keys come
+    // very close in time to a query) are summed bucket by bucket
+    {
+      const int64_t span = max(w_ts_max - kmin, kmax - w_ts_min);
+      const int b_top = min(63 - __builtin_clzll((uint64_t)max(span, (int64_t)0) + 1), n_time_eff - 1);
+      win_fit(max(0, b_top - 7), b_top);
+    }
+    // (a rolled loop over the lane's 32 pairs, 8 at a time, reading dS back
+    // from the block in LDS: this path is rare, and unrolled selects would
+    // hold too many lane masks)
+    auto per_pair = [&](auto small_tag) {
+      constexpr bool SMALL = decltype(small_tag)::value;
+      LB* blk = dl + (wave >> 1) * DS_BLOCK * 2;
+      const int col = (wave & 1) * 32 + (lane & 31);  // this lane's query in the block
+      const uint32_t t_lo = (uint32_t)(uintptr_t)LDS_PTR(const int32_t, st.ts_lo);
+      const uint32_t t64 = (uint32_t)(uintptr_t)LDS_PTR(const int64_t, st.ts64);
+      // pairs e0 .. e0 + 7 of the lane (keys 16 (e / 8) + 8 hl + e mod 8): dS and bucket
+      auto pairs8 = [&](int e0, float (&ds)[8], int (&bkt)[8]) {
+        uint32_t ad[8], at[8], vd[8], vt[8], vh[8];
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int kk = 16 * (e0 >> 3) + 8 * hl + e;
+          ad[e] = (uint32_t)(uintptr_t)blk + ds_chunk_off(kk, col >> 3) + (col & 7) * 2;
+          at[e] = SMALL ? t_lo + 4 * kk : t64 + 8 * kk;
+        }
+        lds_read8_u16(ad, vd);
+        lds_read8_b32(at, vt);
+        if constexpr (!SMALL) {
+          #pragma unroll
+          for (int e = 0; e < 8; ++e) at[e] += 4;
+          lds_read8_b32(at, vh);
+        }
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ds[e] = bf16_bits_to_f32(vd[e]);
+          const int64_t tk = SMALL ? 0 : (int64_t)(((uint64_t)vh[e] << 32) | vt[e]);
+          bkt[e] = min(63 - time_z<SMALL>(tsq, tk, tsq_lo, (int32_t)vt[e]), n_time_eff - 1);
+        }
+      };
+      int b_below = 64;  // lowest bucket of this lane under the window
+      #pragma unroll 1
+      for (int e0 = 0; e0 < 32; e0 += 8) {
+        float ds[8];
+        int bkt[8];
+        pairs8(e0, ds, bkt);
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          win_add(bkt[e], ds[e]);
+          b_below = bkt[e] < wb ? min(b_below, bkt[e]) : b_below;
+        }
+      }
+      for (int m = 32; m >= 1; m >>= 1) b_below = min(b_below, __shfl_xor(b_below, m));
+      for (int b = b_below; b < wb; ++b) {  // wave-uniform, usually empty
+        float x = 0.0f;
+        #pragma unroll 1
+        for (int e0 = 0; e0 < 32; e0 += 8) {
+          float ds[8];
+          int bkt[8];
+          pairs8(e0, ds, bkt);
+          #pragma unroll
+          for (int e = 0; e < 8; ++e) x += bkt[e] == b ? ds[e] : 0.0f;
+        }
+        x = wave_sum_f(x);
+        if (lane == 0) lds_add_f32_unordered(&hist.time[wave][b], x);
+      }
+    };
+    if (small_span) per_pair(std::true_type{});
+    else per_pair(std::false_type{});
+  };
+
+  const int ntiles = k_end > k_begin ? (int)ceil_div(k_end - k_begin, KT) : 0;
+  int64_t tsreg = 0;
+  // Stage of key tile j0: K rows (as stage_rows, clamped to the user's last
+  // row) and the dS blocks (kt, qt0) (waves 0, 1) and (kt, qt0 + 1) (waves
+  // 2, 3), each where it exists; an absent block is never read
+  auto issue = [&](Stage<T, D>& st, int j0) {
+    constexpr int ND = G::TILE / (NWAVES * 1024);
+    const int last = min(KT, L - j0) - 1;
+    const uint32_t rstride = (uint32_t)(H * G::ROWB);
+    const unsigned char* kb = (const unsigned char*)a.k + (((q_off + j0) * H + h) * D) * 2;
+    #pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const int base = (wave * ND + i) * 64;
+      const int P = base + lane;
+      const int r = P / G::CPR, pc = P % G::CPR;
+      const uint32_t off = __umul24((uint32_t)min(r, last), rstride) + (uint32_t)((pc ^ swz_b<D>(r)) << 4);
+      __builtin_amdgcn_global_load_lds((const void*)(kb + off), LDS_PTR(void, st.k + base * 16), 16, 0, 0);
+    }
+    const int kt = j0 / KT;
+    const int64_t gb = blk0 + (int64_t)qt_w * (qt_w + 1) / 2 + kt;
+    if (kt <= qt_w && qt_w < nbb && gb < a.ds_cap) {
+      const unsigned char* src = (const unsigned char*)(a.ds + gb * DS_BLOCK);
+      #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int base = ((wave & 1) * 4 + i) * 64;  // chunk index within the block
+        const int P = base + lane;
+        const int r = P >> 3, pc = P & 7;
+        __builtin_amdgcn_global_load_lds((const void*)(src + ds_chunk_off(r, pc)),
+                                         LDS_PTR(void, st.v + (wave >> 1) * DS_BLOCK * 2 + base * 16), 16, 0, 2);
+      }
+    }
+    if (wave == 0) tsreg = a.ts[q_off + j0 + min(lane, last)];
+  };
+  if (ntiles > 0) {
+    issue(st0, k_begin);
+    finish_stage<D>(st0, tsreg);
+  } else {
+    __syncthreads();
+  }
+  // time classes of the next 64 tiles, lane i for tile t0 + i
+  auto time_batch = [&](int t0) {
+    const int tl = t0 + lane;
+    int c = 255;
+    if (tl < ntiles) {
+      row_time_range(a, q_off + k_begin + tl * KT, tb_mn, tb_mx);
+      c = time_class(tb_mn, tb_mx, w_ts_min, w_ts_max, n_time_eff);
+    }
+    tcls = c;
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    if (has_time && (t & 63) == 0) time_batch(t);
+    const int j0 = k_begin + t * KT;
+    if (t + 1 < ntiles) issue(st1, j0 + KT);
+    compute_tile(st0, j0, t);
+    if (t + 1 >= ntiles) break;
+    finish_stage<D>(st1, tsreg);
+    if (t + 2 < ntiles) issue(st0, j0 + 2 * KT);
+    compute_tile(st1, j0 + KT, t + 1);
+    if (t + 2 < ntiles) finish_stage<D>(st0, tsreg);
+  }
+
+  if (w_rows) {
+    if (has_time) {
+      fold_time();
+      flush_win();
+    }
+    if (has_pos) {
+      const float x = wave_sum_f((hl == 0 ? pos_acc[0] : 0.0f) + pos_far);
+      if (lane == 0) lds_add_f32_unordered(&hist.pos[wave][n_pos - 1], x);
+    }
+  }
+  store_rows_t<D>(dqacc, a.alpha / (float)n_norm, st0, st1, a.dq, q_off + q_start, q_len, h, H);
+
+  // per-item bias gradients (scaled by 1 / N) in the slot of the item's
+  // canonical index, as the four-wave kernel writes them
+  const int64_t tiles = ldc(a.prefix + a.B) / H;
+  const int64_t canon = (int64_t)h * tiles + ldc(a.prefix + b) / H + q_start / QT;
+  float* part = a.rab_part + canon * RAB_SLOTS;
+  const float inv_n = 1.0f / (float)n_norm;
+  if (has_pos) {
+    for (int i = tid; i < n_pos; i += NTHREADS) {
+      float x = 0.0f;
+      #pragma unroll
+      for (int w = 0; w < NWAVES; ++w) x += hist.pos[w][i];
+      part[i] = x * inv_n;
+    }
+  }
+  if (has_time && tid < 64) {
+    float x = 0.0f;
+    #pragma unroll
+    for (int w = 0; w < NWAVES; ++w) x += hist.time[w][tid];
+    part[BWD_MAX_NPOS + tid] = x * inv_n;
+  }
+}
+
+// ============================================================================
 // Bias-table gradients: add the per-item histograms in canonical order
 // ============================================================================
 // Block (x, y): 64 buckets of table row y (a head, or the one shared row;
@@ -1452,29 +1639,14 @@ __global__ __launch_bounds__(64 * RAB_GROUPS) void rab_reduce_kernel(RabReduceAr
   }
 }
 
-// Which dQ kernel for d = 128. Measured on 8 x 8,192 and on the jagged
-// training shape, the eight-wave kernel (one workgroup per CU) costs about
-// 1.22x the four-wave one (two per CU) per unit of work, but finishes an
-// item's chain of key tiles in about 0.6x the time. So it wins when the
-// longest chain, not the total work, sets the launch's time: with W the work
-// in 128-row x 64-key tiles and C the longest chain in key tiles, when
-// W / 512 < 0.82 C, i.e. W < 420 C. W is estimated from what the host knows,
-// max(T^2 / B, max_len^2) * H / (128 * 64) (the first term is exact for equal
-// lengths, the second for one long user); C = ceil(max_len / 64).
-bool bwd_dq_eight_waves(const BwdArgs& a, int max_len) {
-  const double T = (double)a.T, B = (double)std::max(1, a.B), L = (double)max_len;
-  const double work = std::max(T * T / B, L * L) * a.H / (double)(QT * KT);
-  const double chain = std::ceil(L / KT);
-  return work < 400.0 * chain;
-}
-
-hipError_t launch_attn_bwd(const BwdArgs& a, int D, int64_t grid, int max_len, hipStream_t s) {
+hipError_t launch_attn_bwd(const BwdArgs& a, int D, int64_t grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid), blk(NTHREADS);
   if (D == 128) {
-    if (bwd_dq_eight_waves(a, max_len)) hipLaunchKernelGGL(attn_bwd_dq8_kernel, g, dim3(DQ8_THREADS), 0, s, a);
-    else hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, g, blk, 0, s, a);
+    // dK and dV first: that kernel writes the dS blocks the dQ kernel reads
+    if (!a.ds || !a.ds_prefix) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_bwd_dkdv8_kernel, g, dim3(DKDV8_THREADS), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dq_ds_kernel, g, blk, 0, s, a);
   } else if (D == 64) {
     hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, g, blk, 0, s, a);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, g, blk, 0, s, a);

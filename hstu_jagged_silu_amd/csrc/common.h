@@ -59,8 +59,10 @@ struct WsLayout {
   int64_t max_items;
   int32_t n_chunks;       // key splits (1 except on the cached path)
   int32_t chunk_keys;     // keys per split (multiple of KT)
-  // backward only: dO (bf16), bias-table gradient partials, affine partials
-  size_t dout_off, rab_off, lnp_off;
+  // backward only: dO (bf16), bias-table gradient partials, affine partials,
+  // and for d = 128 the dS blocks and their per-user prefix
+  size_t dout_off, rab_off, lnp_off, ds_off, dsp_off;
+  int64_t ds_blocks;      // capacity of the dS region in 64 x 64 blocks (0: none)
   int32_t ln_waves;
 };
 

@@ -67,6 +67,9 @@ struct SchedArgs {
   const int64_t* ts_pages;       // cached
   const int32_t* page_table;
   int32_t num_pages, max_pages, stat_stride;
+  // backward, d = 128: per-user prefix of the dS blocks (64 x 64, causal:
+  // nb (nb + 1) / 2 per head, nb = ceil(L / 64)), [B+1]; null elsewhere
+  int64_t* ds_prefix;
 };
 
 // Arguments of the LayerNorm + U gating epilogue (sums key splits first).
@@ -166,6 +169,13 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* rab_part;               // [items][RAB_SLOTS]
+  // d = 128: dS of every causal 64 x 64 (key, query) block, bf16 [key][query],
+  // written by the dK/dV kernel and read by the dQ kernel; block (kt, qt) of
+  // user b and head h at (H * ds_prefix[b] + h * nb (nb + 1) / 2 + qt (qt + 1)
+  // / 2 + kt) * 4096 elements
+  bf16* ds;
+  const int64_t* ds_prefix;
+  int64_t ds_cap;                // blocks the region holds; a block past it is neither written nor read
 };
 
 struct RabReduceArgs {
@@ -204,9 +214,7 @@ hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int mode, int64_t gr
 hipError_t launch_ln_gate(const LnArgs& a, int dtype, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_ln_bwd(const LnBwdArgs& a, hipStream_t s);       // rows, then the affine reduce
-hipError_t launch_attn_bwd(const BwdArgs& a, int D, int64_t grid, int max_len, hipStream_t s);
-// true when d = 128 takes the eight-wave dQ kernel (latency-bound launches)
-bool bwd_dq_eight_waves(const BwdArgs& a, int max_len);
+hipError_t launch_attn_bwd(const BwdArgs& a, int D, int64_t grid, hipStream_t s);
 hipError_t launch_rab_reduce(const RabReduceArgs& a, hipStream_t s);
 
 }  // namespace hstu

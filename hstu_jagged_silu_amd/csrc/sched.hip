@@ -142,20 +142,21 @@ __device__ inline int item_bin(const SchedArgs& a, const WorkItem& w) {
 // Block-wide exclusive scan of one value per thread; returns the block
 // total. Shuffle scan inside each wave, then every thread adds the totals of
 // the waves before its own: two barriers in all.
-__device__ inline int block_scan(int x, int* wsum, int& excl) {
+template <typename V>
+__device__ inline V block_scan(V x, V* wsum, V& excl) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = x;
+  V inc = x;
   #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(inc, off);
+    const V y = __shfl_up(inc, off);
     if (lane >= off) inc += y;
   }
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
-  int before = 0, total = 0;
+  V before = 0, total = 0;
   #pragma unroll
   for (int w = 0; w < SCHED_WAVES; ++w) {
-    const int t = wsum[w];
+    const V t = wsum[w];
     before += w < wave ? t : 0;
     total += t;
   }
@@ -212,6 +213,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(SchedArgs a) {
     return;
   }
   __shared__ int wsum[SCHED_WAVES];
+  __shared__ long long wsum64[SCHED_WAVES];
   __shared__ int hist[NBINS];
   __shared__ int start[NBINS];
   __shared__ int s_pref[LDS_USERS + 1];
@@ -220,15 +222,20 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(SchedArgs a) {
   const bool in_lds = a.B <= LDS_USERS;
   for (int i = tid; i < NBINS; i += SCHED_THREADS) hist[i] = 0;
 
-  // 1. items per user -> exclusive prefix over users
+  // 1. items per user -> exclusive prefix over users (and, for the
+  // backward at d = 128, the prefix of the users' dS blocks)
   int carry = 0;
+  long long ds_carry = 0;
   for (int base = 0; base < a.B; base += SCHED_THREADS) {
     const int b = base + tid;
     int c = 0;
+    long long c2 = 0;
     if (b < a.B) {
       const UserRaw r = user_raw(a, b);
       if (in_lds) s_raw[b] = r;
       c = a.H * user_items_per_head(a, user_geo(a, r));
+      const long long nb = ceil_div(r.L, KT);
+      c2 = nb * (nb + 1) / 2;
     }
     int excl;
     const int tot = block_scan(c, wsum, excl);
@@ -237,7 +244,14 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(SchedArgs a) {
       if (in_lds) s_pref[b] = carry + excl;
     }
     carry += tot;
+    if (a.ds_prefix) {  // a kernel argument: every thread takes the same branch
+      long long excl2;
+      const long long tot2 = block_scan(c2, wsum64, excl2);
+      if (b < a.B) a.ds_prefix[b] = ds_carry + excl2;
+      ds_carry += tot2;
+    }
   }
+  if (a.ds_prefix && tid == 0) a.ds_prefix[a.B] = ds_carry;
   int total = carry;
   if ((int64_t)total > a.max_items) total = (int)a.max_items;  // cannot happen with a valid bound
   if (tid == 0) {

@@ -249,6 +249,12 @@ typedef struct {
  * between forward and backward).
  *   arguments as hstu_attn_fwd, plus dy [T, H*d] and grads (see above)
  *   ws, ws_bytes  workspace of at least hstu_workspace_size(HSTU_FN_FULL_BWD, ...)
+ * For head_dim 128 the workspace also holds the bf16 gradient of the scores
+ * of every causal 64 x 64 (key, query) block, written by the dK/dV pass and
+ * read by the dQ pass (about H * sum_b L_b^2 bytes, sized from batch,
+ * total_tokens and max_len). There max_len must bound every L_b: a longer
+ * user leaves the gradients unspecified (debug mode reports it) while no
+ * memory outside the given buffers is read or written.
  * bf16 only (HSTU_ERR_UNSUPPORTED for fp32) and n_pos <= 512. Outputs must
  * not alias inputs. All tensors 16-byte aligned. Results do not depend on
  * scheduling: every sum runs in a fixed order. params->timing_events, if
