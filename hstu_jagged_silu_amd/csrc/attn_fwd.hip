@@ -282,10 +282,18 @@ void attn_fwd_kernel(AttnArgs a) {
   // inside one power of two, or the clamped last bucket), NaN where the
   // bucket varies. One lane-parallel pass replaces a per-tile scalar
   // classification (range loads, 64-bit compares, clz, table read).
-  float tc = 0.0f;
+  // Two-bucket tiles (queries after keys, |dt| range crossing one power of
+  // two, every |dt| below 2^31 - 2) also carry their threshold 2^b - 1 and
+  // the two table values, so that such a tile needs no range loads either
+  // and picks its bucket with one 32-bit subtract per element; tthr < 0
+  // marks every other tile.
+  float tc = 0.0f, tclo = 0.0f, tchi = 0.0f;
+  int tthr = -1;
   auto time_batch = [&](int t0, int ntiles) {
     const int t = t0 + lane;
     float c = __builtin_nanf("");
+    float clo = 0.0f, chi = 0.0f;
+    int thr = -1;
     if (t < ntiles) {
       const int j0 = k_begin + t * KT;
       int64_t kmin, kmax;
@@ -306,10 +314,20 @@ void attn_fwd_kernel(AttnArgs a) {
       if (lo >= 0) {
         const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
         const int blo = min(63 - zlo, n_time_eff - 1), bhi = min(63 - zhi, n_time_eff - 1);
-        if (blo == bhi) c = tab.time_t[zlo];
+        if (blo == bhi) {
+          c = tab.time_t[zlo];
+        } else if (w_ts_min >= kmax && zhi == zlo - 1 && 63 - zhi <= n_time_eff - 1 &&
+                   hi < ((int64_t)1 << 31) - 2) {
+          thr = (1 << (63 - zhi)) - 1;  // |dt| >= thr selects the upper bucket
+          clo = tab.time_t[zlo];
+          chi = tab.time_t[zhi];
+        }
       }
     }
     tc = c;
+    tclo = clo;
+    tchi = chi;
+    tthr = thr;
   };
 
   auto compute_tile = [&](Stage<T, D>& st, int j0, int t) {
@@ -320,10 +338,12 @@ void attn_fwd_kernel(AttnArgs a) {
     const bool pos_uniform = (a.pos_tab == nullptr) || (w_p_min - (j0 + KT - 1) >= n_pos - 1);
     bool time_uniform = !has_time;
     float c_time = 0.0f;
+    int two_thr_t = -1;  // >= 0: a two-bucket tile classified by the batch pass
     if (has_time) {
       const float ct = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tc), t & 63));
       time_uniform = ct == ct;  // NaN: the bucket varies over the tile
       c_time = time_uniform ? ct : 0.0f;
+      if (!time_uniform) two_thr_t = __builtin_amdgcn_readlane(tthr, t & 63);
     }
     const bool uniform = pos_uniform && time_uniform;
     const float c_pos = a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f;
@@ -473,6 +493,19 @@ void attn_fwd_kernel(AttnArgs a) {
         for (int v = 0; v < 16; ++v) {
           y0[v] = fmaf(s0[v], sc, cu);
           y1[v] = fmaf(s1[v], sc, cu);
+          asm volatile("" : "+v"(y0[v]), "+v"(y1[v]));
+        }
+      } else if (two_thr_t >= 0 && pos_uniform && !need_mask) {
+        // x = dt - thr in 32 bits (exact: 0 <= dt < 2^31 - 2), upper bucket iff x >= 0
+        const float clo = c_pos + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tclo), t & 63));
+        const float chi = c_pos + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tchi), t & 63));
+        const uint32_t b_lane = (uint32_t)tsq_lo - (uint32_t)two_thr_t;
+        #pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int32_t x0 = (int32_t)(b_lane - (uint32_t)ts_lo_l[M::key_of(0, v, 0)]);
+          const int32_t x1 = (int32_t)(b_lane - (uint32_t)ts_lo_l[M::key_of(1, v, 0)]);
+          y0[v] = fmaf(s0[v], sc, x0 >= 0 ? chi : clo);
+          y1[v] = fmaf(s1[v], sc, x1 >= 0 ? chi : clo);
           asm volatile("" : "+v"(y0[v]), "+v"(y1[v]));
         }
       } else {
