@@ -83,6 +83,16 @@ def test_unordered_and_huge_timestamps():
     check(run_full(inp), oracle_full(inp), "bf16", "huge ts")
 
 
+def test_time_bucket_edges_unit_gap():
+    """Timestamps one second apart: |dt| is the distance, so every row has
+    pairs exactly at a time bucket's lower edge 2^b - 1, most of them in key
+    tiles that span two buckets (the threshold path of the kernel); the time
+    table is scaled so that a pair in the wrong bucket shows (a CPU pin
+    plants that mistake in the oracle and sees it)."""
+    inp = W.time_bucket_edges()
+    check(run_full(inp), oracle_full(inp), "bf16", "time bucket edges")
+
+
 def test_maximum_sizes_sampled_rows():
     """The largest supported shapes: H*d = 2,048 (16 heads of 128), a 2,048-entry
     position table, 64 time buckets, users longer than the position table."""

@@ -12,7 +12,9 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle.hstu as oracle_hstu
 import workloads as W
+from tolerances import TOL
 
 
 def _rand_case(rng, lengths, H, d, n_pos=5, n_time=6, per_head=False, ts_spread=50):
@@ -546,3 +548,24 @@ def test_dense_matches_loops_and_split_order():
     for i, blk in enumerate(blocks):
         expect = [[x / (1 + math.exp(-x)) for x in row] for row in ref[:, 2 * i:2 * i + 2]]
         np.testing.assert_allclose(blk, expect, rtol=1e-15, atol=1e-300)
+
+
+def test_time_bucket_edge_input_detects_a_shifted_edge(monkeypatch):
+    """The GPU test on workloads.time_bucket_edges can see a kernel that puts
+    pairs at a bucket's lower edge (|dt| = 2^b - 1, b >= 7: only in key tiles
+    away from the diagonal) one bucket too low: planted in the oracle, that
+    mistake moves the output by more than four times the bf16 bar."""
+    inp = W.time_bucket_edges()
+    args = (inp.q, inp.k, inp.v, inp.u, inp.ts, inp.seq_offsets, inp.tables.pos, inp.tables.time)
+    y_ok, _ = oracle.hstu_full(*args)
+    right = oracle_hstu.time_bucket
+
+    def shifted(dt, n_time):
+        a = np.abs(np.asarray(dt, dtype=np.int64))
+        b = right(dt, n_time)
+        x = a + 1
+        return np.where((a >= 64) & ((x & (x - 1)) == 0), b - 1, b)
+
+    monkeypatch.setattr(oracle_hstu, "time_bucket", shifted)
+    y_bad, _ = oracle.hstu_full(*args)
+    assert oracle.max_rel_row_error(y_bad, y_ok) > 4 * TOL["bf16"]

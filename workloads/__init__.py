@@ -158,6 +158,21 @@ def long_seq(seed: int = 6, batch: int = 8, seq_len: int = 8192) -> JaggedInputs
     return _jagged_from_rng(f"causal_B{batch}_L{seq_len}_H4_d128_bf16", rng, lengths, 4, 128, "bf16", 128, 128)
 
 
+def time_bucket_edges(seed: int = 91) -> JaggedInputs:
+    """Edge case for the time buckets: users of 300, 200 and 257 tokens one
+    second apart, so |dt| equals the distance and every bucket's lower edge
+    |dt| = 2^b - 1 occurs in every row that reaches it; 2 heads of 64, bf16,
+    4 position buckets (constant beyond distance 3), 16 time buckets, the
+    time table scaled by 16 so that a pair in the wrong bucket moves the
+    output well past the bf16 bar."""
+    inp = jagged("time_bucket_edges", seed, [300, 200, 257], 2, 64, "bf16", 4, 16)
+    off = inp.seq_offsets
+    for b in range(len(off) - 1):
+        inp.ts[off[b]:off[b + 1]] = TS_START + np.arange(off[b + 1] - off[b], dtype=np.int64)
+    inp.tables.time = (inp.tables.time * 16).astype(np.float32)
+    return inp
+
+
 @dataclasses.dataclass
 class CachedInputs:
     """KV-cache delta workload: per user a cached prefix and some new tokens.
