@@ -56,21 +56,25 @@ __device__ inline int time_z(int64_t ta, int64_t tb, int32_t ta_lo, int32_t tb_l
 // wave's own minimum) against the wave's own [w_min, w_max]. Bits 0..6:
 // z = clz64(|dt| + 1) when every pair of the tile falls in one (clamped)
 // time bucket, else 127; bit 7: every |dt| stays below 2^31 - 2, so the
-// 32-bit bucket form is exact. A wave computes it for 64 tiles at a time,
-// lane i for tile t0 + i, and each tile reads its class with one readlane.
+// 32-bit bucket form is exact; bit 8: the other side's times all follow the
+// wave's and the pairs span exactly two unclamped buckets, the upper one
+// b in bits 9..14 (a pair is in b iff its dt >= 2^b - 1). A wave computes
+// it for 64 tiles at a time, lane i for tile t0 + i, and each tile reads
+// its class with one readlane.
 __device__ inline int time_class(int64_t o_min, int64_t o_max, int64_t w_min, int64_t w_max, int n_time_eff) {
   if (o_min > o_max) o_min = o_max = w_min;
   const int64_t d1 = w_max - o_min, d2 = o_max - w_min;
   const bool small = max(d1 < 0 ? -d1 : d1, d2 < 0 ? -d2 : d2) < ((int64_t)1 << 31) - 2;
-  int z = 127;
+  int z = 127, two = 0;
   int64_t lo = -1, hi = -1;
   if (w_min >= o_max) { lo = w_min - o_max; hi = w_max - o_min; }
   else if (o_min >= w_max) { lo = o_min - w_max; hi = o_max - w_min; }
   if (lo >= 0) {
     const int zlo = __builtin_clzll((uint64_t)lo + 1), zhi = __builtin_clzll((uint64_t)hi + 1);
     if (min(63 - zlo, n_time_eff - 1) == min(63 - zhi, n_time_eff - 1)) z = zlo;
+    else if (small && o_min >= w_max && zhi == zlo - 1 && 63 - zhi <= n_time_eff - 1) two = 256 | ((63 - zhi) << 9);
   }
-  return (small ? 128 : 0) | z;
+  return (small ? 128 : 0) | z | two;
 }
 
 // Timestamp range (conservative superset) of the packed rows r0 .. r0 + 63,
@@ -89,7 +93,7 @@ __device__ inline int64_t readlane64(int64_t x, int l) {
 // Unpacks a tile's time class (see time_class) for the wave-uniform tile t.
 __device__ inline void tile_class(int tcls, int t, bool& time_uniform, int& z_tile, bool& small_span) {
   const int c = __builtin_amdgcn_readlane(tcls, t & 63);
-  small_span = c >= 128;
+  small_span = (c & 128) != 0;
   time_uniform = (c & 127) != 127;
   if (time_uniform) z_tile = c & 127;
 }
@@ -918,6 +922,13 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
     bool small_span = true;
     if (has_time) tile_class(tcls, t, time_uniform, z_tile, small_span);
     const bool fast = pos_uniform && time_uniform && !need_mask;
+    // two time buckets (queries after this wave's keys), constant position
+    // bias, no mask: bucket by one 32-bit subtract per pair
+    int two_b = -1;
+    if (has_time && !fast && pos_uniform && !need_mask) {
+      const int c = __builtin_amdgcn_readlane(tcls, t & 63);
+      if (c & 256) two_b = (c >> 9) & 63;
+    }
     const float c_uni = (a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f) + (has_time ? tab.time_t[z_tile] : 0.0f);
     const int64_t* ts_l = st.ts64 + M::HLK * hl;
     const int32_t* tsl_lo = st.ts_lo + M::HLK * hl;
@@ -955,6 +966,20 @@ __global__ __launch_bounds__(DKDV8_THREADS, 2) void attn_bwd_dkdv8_kernel(BwdArg
       for (int v = 0; v < 16; ++v) {
         float p, ds;
         silu_fwd_bwd(fmaf(s[v], sc, c_uni), dp[v], p, ds);
+        pb[v >> 3][v & 7] = (bf16)p;
+        dsb[v >> 3][v & 7] = (bf16)ds;
+      }
+    } else if (two_b >= 0) {
+      // x = (t_q - t_k) - (2^b - 1) in 32 bits (exact: 0 <= dt < 2^31 - 2);
+      // the pair is in bucket b iff x >= 0, else in b - 1
+      const float c_pos = a.pos_tab ? tab.pos_t[n_pos - 1] : 0.0f;
+      const float c_hi = c_pos + tab.time_t[63 - two_b], c_lo = c_pos + tab.time_t[64 - two_b];
+      const uint32_t b_lane = (uint32_t)tsk_lo + (uint32_t)((1 << two_b) - 1);
+      #pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int32_t x = (int32_t)((uint32_t)tsl_lo[M::key_of(qb, v, 0)] - b_lane);
+        float p, ds;
+        silu_fwd_bwd(fmaf(s[v], sc, x >= 0 ? c_hi : c_lo), dp[v], p, ds);
         pb[v >> 3][v & 7] = (bf16)p;
         dsb[v >> 3][v & 7] = (bf16)ds;
       }
