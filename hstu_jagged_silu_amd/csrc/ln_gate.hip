@@ -5,8 +5,10 @@
 // partial sums over key splits; they are added here, in split order, first.
 //
 // One wave64 per token row. Every global access is a contiguous row segment
-// (16 bytes of O per lane, 8 or 16 bytes of U and Y), and all loads of a row
-// are issued before the first reduction so that they overlap. HBM-bound: per
+// (16 bytes of O per lane, 8 or 16 bytes of U and Y; the norm-ready form
+// reads 16 bytes of deviations and of U per lane where the row width allows),
+// and all loads of a row are issued before the first reduction so that they
+// overlap. HBM-bound: per
 // element it reads 4 bytes of O per split plus U and writes Y. A second form
 // finishes the attention kernel's norm-ready store (bf16 deviations and
 // per-head statistics) with 2 bytes of O per element.
@@ -162,12 +164,29 @@ __global__ __launch_bounds__(64 * LN_ROWS) void ln_gate_kernel(LnArgs a) {
 // y = ((dev + mean_h - mean) / sqrt(M2 / HD + eps) * w + b) * u.
 // Reads 2 bytes of deviation per element (and 8 bytes per head) instead of
 // 4 bytes of O.
-template <int NCH, bool FULL_LANES>
+template <int CW>
+__device__ inline void load_bf16(const bf16* p, float (&x)[CW]) {
+  if constexpr (CW == 8) {
+    const bf16x8 v = *(const bf16x8*)p;
+    #pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+  } else {
+    const bf16x4 v = *(const bf16x4*)p;
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = (float)v[e];
+  }
+}
+
+// NCH chunks of CW values per lane (CW = 8: 16-byte accesses, for rows of a
+// multiple of 512 values; CW = 4: 8-byte accesses, H*d = 256 * NCH when
+// FULL_LANES, else the row has fewer than 256 * NCH values and trailing
+// lanes idle). A chunk lies inside one head (head_dim is a multiple of CW).
+template <int NCH, bool FULL_LANES, int CW>
 __global__ __launch_bounds__(64 * LN_ROWS) void ln_gate_dev_kernel(LnArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * LN_ROWS + (threadIdx.x >> 6);
   if (row >= a.T) return;
-  const int nch = a.HD / 4;
+  const int nch = a.HD / CW;
   const int H = a.HD / a.head_dim;
 
   bool on[NCH];
@@ -176,16 +195,16 @@ __global__ __launch_bounds__(64 * LN_ROWS) void ln_gate_dev_kernel(LnArgs a) {
   for (int i = 0; i < NCH; ++i) {
     const int c = lane + 64 * i;
     on[i] = FULL_LANES || c < nch;
-    col[i] = 4 * (FULL_LANES ? c : min(c, nch - 1));
+    col[i] = CW * (FULL_LANES ? c : min(c, nch - 1));
   }
   const bf16* drow = a.o_dev + row * a.HD;
   const bf16* urow = (const bf16*)a.u + row * a.HD;
   const float* srow = a.o_stats + 2 * row * H;
-  f32x4 z[NCH], u[NCH];
+  float z[NCH][CW], u[NCH][CW];
   #pragma unroll
-  for (int i = 0; i < NCH; ++i) z[i] = load4(drow + col[i]);
+  for (int i = 0; i < NCH; ++i) load_bf16<CW>(drow + col[i], z[i]);
   #pragma unroll
-  for (int i = 0; i < NCH; ++i) u[i] = load4(urow + col[i]);
+  for (int i = 0; i < NCH; ++i) load_bf16<CW>(urow + col[i], u[i]);
   float mh[NCH];
   #pragma unroll
   for (int i = 0; i < NCH; ++i) mh[i] = srow[2 * (col[i] / a.head_dim)];
@@ -200,30 +219,45 @@ __global__ __launch_bounds__(64 * LN_ROWS) void ln_gate_dev_kernel(LnArgs a) {
   #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     if (!on[i]) continue;
-    f32x4 w = {1, 1, 1, 1}, bb = {0, 0, 0, 0};
-    if (a.ln_w) w = *(const f32x4*)(a.ln_w + col[i]);
-    if (a.ln_b) bb = *(const f32x4*)(a.ln_b + col[i]);
     const float shift = mh[i] - mean;
-    f32x4 yv;
+    float yv[CW];
     #pragma unroll
-    for (int e = 0; e < 4; ++e) yv[e] = fmaf((z[i][e] + shift) * rstd, w[e], bb[e]) * u[i][e];
-    store4(yrow + col[i], yv);
+    for (int e0 = 0; e0 < CW; e0 += 4) {
+      f32x4 w = {1, 1, 1, 1}, bb = {0, 0, 0, 0};
+      if (a.ln_w) w = *(const f32x4*)(a.ln_w + col[i] + e0);
+      if (a.ln_b) bb = *(const f32x4*)(a.ln_b + col[i] + e0);
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) yv[e0 + e] = fmaf((z[i][e0 + e] + shift) * rstd, w[e], bb[e]) * u[i][e0 + e];
+    }
+    if constexpr (CW == 8) {
+      bf16x8 v;
+      #pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (bf16)yv[e];
+      *(bf16x8*)(yrow + col[i]) = v;
+    } else {
+      bf16x4 v;
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (bf16)yv[e];
+      *(bf16x4*)(yrow + col[i]) = v;
+    }
   }
 }
 
 static void launch_dev(const LnArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div(a.T, LN_ROWS)), blk(64 * LN_ROWS);
-  switch (a.HD) {
-    case 256: hipLaunchKernelGGL((ln_gate_dev_kernel<1, true>), grid, blk, 0, s, a); return;
-    case 512: hipLaunchKernelGGL((ln_gate_dev_kernel<2, true>), grid, blk, 0, s, a); return;
-    case 1024: hipLaunchKernelGGL((ln_gate_dev_kernel<4, true>), grid, blk, 0, s, a); return;
-    case 2048: hipLaunchKernelGGL((ln_gate_dev_kernel<8, true>), grid, blk, 0, s, a); return;
+  if (a.head_dim % 8 == 0) {  // 16-byte accesses
+    switch (a.HD) {
+      case 512: hipLaunchKernelGGL((ln_gate_dev_kernel<1, true, 8>), grid, blk, 0, s, a); return;
+      case 1024: hipLaunchKernelGGL((ln_gate_dev_kernel<2, true, 8>), grid, blk, 0, s, a); return;
+      case 2048: hipLaunchKernelGGL((ln_gate_dev_kernel<4, true, 8>), grid, blk, 0, s, a); return;
+    }
   }
+  if (a.HD == 256) { hipLaunchKernelGGL((ln_gate_dev_kernel<1, true, 4>), grid, blk, 0, s, a); return; }
   const int nch = (int)ceil_div(a.HD / 4, 64);
-  if (nch <= 1) hipLaunchKernelGGL((ln_gate_dev_kernel<1, false>), grid, blk, 0, s, a);
-  else if (nch <= 2) hipLaunchKernelGGL((ln_gate_dev_kernel<2, false>), grid, blk, 0, s, a);
-  else if (nch <= 4) hipLaunchKernelGGL((ln_gate_dev_kernel<4, false>), grid, blk, 0, s, a);
-  else hipLaunchKernelGGL((ln_gate_dev_kernel<8, false>), grid, blk, 0, s, a);
+  if (nch <= 1) hipLaunchKernelGGL((ln_gate_dev_kernel<1, false, 4>), grid, blk, 0, s, a);
+  else if (nch <= 2) hipLaunchKernelGGL((ln_gate_dev_kernel<2, false, 4>), grid, blk, 0, s, a);
+  else if (nch <= 4) hipLaunchKernelGGL((ln_gate_dev_kernel<4, false, 4>), grid, blk, 0, s, a);
+  else hipLaunchKernelGGL((ln_gate_dev_kernel<8, false, 4>), grid, blk, 0, s, a);
 }
 
 template <typename T>
