@@ -448,6 +448,16 @@ def _bench_backward(torch, hs, W, inp, steps, warmup):
     pairs = H * hs.pair_count("full", [int(x) for x in inp.lengths])
     bwd_flop = 5 * 2 * d * pairs      # S recomputed, dP, dV, dQ, dK: five products of 2*d FLOP per pair
     fwd_ms, ln_ms, attn_ms = mean_span(evs, 0, 1), mean_span(evs, 1, 2), mean_span(evs, 2, 3)
+    # the same backward on the forward's workspace (HSTU_FLAG_SAVED_FORWARD):
+    # no recomputed forward, the norm backward reads the forward's norm-ready store
+    ps = hs.LayerParams(num_heads=H, head_dim=d, dtype=bf, pos_tab=p.pos_tab, time_tab=p.time_tab, ln_w=p.ln_w,
+                        ln_b=p.ln_b, flags=hs.HSTU_FLAG_SAVED_FORWARD)
+    hs.hstu_attn_fwd(q, k, v, u, ts, off, inp.max_len, ps, workspace=ws)
+    fn_s = lambda ev: hs.hstu_attn_bwd(q, k, v, u, ts, off, inp.max_len, dy, ps, workspace=ws, timing_events=ev)
+    ms_s, evs_s = timed(fn_s, steps, 0, torch)
+    saved = {"ms_per_step": round(ms_s, 4), "schedule_ms": round(mean_span(evs_s, 0, 1), 4),
+             "norm_backward_ms": round(mean_span(evs_s, 1, 2), 4),
+             "attention_backward_ms": round(mean_span(evs_s, 2, 3), 4)}
     return {
         "workload": inp.name,
         "total_tokens": inp.total,
@@ -459,6 +469,7 @@ def _bench_backward(torch, hs, W, inp, steps, warmup):
         "attention_backward_pct_bf16_peak": round(100 * bwd_flop / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "algorithmic_gflop": round(bwd_flop / 1e9, 3),
         "norm_backward_gbs": round(inp.total * H * d * (4 + 2 + 2 + 2 + 2) / (ln_ms * 1e-3) / 1e9, 1),
+        "saved_forward": saved,
     }
 
 

@@ -30,6 +30,7 @@ HSTU_F32, HSTU_BF16 = 0, 1
 HSTU_FN_FULL, HSTU_FN_CACHED, HSTU_FN_MFALCON, HSTU_FN_MFALCON_CACHED, HSTU_FN_FULL_BWD = 0, 1, 2, 3, 4
 PAGE_SIZE = 64
 HSTU_FLAG_FP32_NORM_INPUT = 1
+HSTU_FLAG_SAVED_FORWARD = 2
 
 EXPORTED_SYMBOLS = (
     "hstu_status_string", "hstu_version", "hstu_workspace_size", "hstu_attn_fwd",
@@ -169,7 +170,8 @@ class LayerParams:
     ln_w: Optional[torch.Tensor] = None
     ln_b: Optional[torch.Tensor] = None
     ln_eps: float = 1e-5
-    flags: int = 0   # HSTU_FLAG_FP32_NORM_INPUT: fp32 attention output round trip instead of the norm-ready store
+    flags: int = 0   # HSTU_FLAG_FP32_NORM_INPUT: fp32 attention output round trip instead of the norm-ready store;
+    #                  HSTU_FLAG_SAVED_FORWARD: hstu_attn_bwd reuses the matching forward's workspace
 
     def c_struct(self, timing_events=None) -> _Params:
         p = _Params()
@@ -303,7 +305,15 @@ def hstu_attn_bwd(q, k, v, u, ts, seq_offsets, max_len: int, dy, params: LayerPa
     Returns a dict with dq, dk, dv ([T, H, d], bf16), du ([T, H*d], bf16),
     d_pos_tab / d_time_tab (fp32, shaped like the tables; None without a
     table or when table_grads is False) and d_ln_w / d_ln_b (fp32 [H*d]; None
-    without the affine term or when affine_grads is False)."""
+    without the affine term or when affine_grads is False).
+
+    With HSTU_FLAG_SAVED_FORWARD in params.flags, workspace must be the one
+    that hstu_attn_fwd used with these same arguments (allocate it with
+    hstu_workspace_size(HSTU_FN_FULL_BWD, ...) and pass it to both calls,
+    with nothing else using it in between): the backward then reuses that
+    forward's norm-ready output instead of recomputing the attention."""
+    if (params.flags & HSTU_FLAG_SAVED_FORWARD) and workspace is None:
+        raise ValueError("HSTU_FLAG_SAVED_FORWARD needs the forward call's workspace")
     _jagged_checks(params, q, k, v, u, ts, seq_offsets)
     _device_tensor(dy, params.dtype, "dy")
     if dy.shape != u.shape:

@@ -70,7 +70,7 @@ hstu_status_t check_params(const hstu_params_t* p) {
     if (p->time_head_stride != 0 && p->time_head_stride < p->n_time) return HSTU_ERR_INVALID_ARG;
   }
   if ((p->ln_w && !aligned16(p->ln_w)) || (p->ln_b && !aligned16(p->ln_b))) return HSTU_ERR_INVALID_ARG;
-  if (p->flags & ~HSTU_FLAG_FP32_NORM_INPUT) return HSTU_ERR_INVALID_ARG;
+  if (p->flags & ~(HSTU_FLAG_FP32_NORM_INPUT | HSTU_FLAG_SAVED_FORWARD)) return HSTU_ERR_INVALID_ARG;
   return HSTU_OK;
 }
 
@@ -337,6 +337,9 @@ hstu_status_t hstu_attn_bwd(const hstu_params_t* params, int32_t batch, const in
   if (params->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
   if (params->pos_tab && params->n_pos > BWD_MAX_NPOS) return HSTU_ERR_UNSUPPORTED;
   if (batch < 0 || total_tokens < 0 || max_len < 0 || !grads) return HSTU_ERR_INVALID_ARG;
+  // saved forward: the workspace holds the norm-ready store of the matching forward call
+  const bool saved = (params->flags & HSTU_FLAG_SAVED_FORWARD) != 0;
+  if (saved && (params->flags & HSTU_FLAG_FP32_NORM_INPUT)) return HSTU_ERR_INVALID_ARG;
   if ((grads->d_pos_tab && !params->pos_tab) || (grads->d_time_tab && !params->time_tab) ||
       (grads->d_ln_w && !params->ln_w) || (grads->d_ln_b && !params->ln_b))
     return HSTU_ERR_INVALID_ARG;
@@ -357,7 +360,9 @@ hstu_status_t hstu_attn_bwd(const hstu_params_t* params, int32_t batch, const in
   };
   const int HD = params->num_heads * params->head_dim;
 
-  // 1. recompute the attention output O (fp32, in the workspace)
+  // 1. recompute the attention output O (fp32, in the workspace), unless the
+  // forward's norm-ready store is there (the schedule is built either way:
+  // the backward kernels read its work list and dS block prefix)
   SchedArgs s = sched_args(MODE_FULL, params, w, ws, batch, seq_offsets, max_len);
   s.ts = ts;
   s.Tk = total_tokens;
@@ -373,12 +378,17 @@ hstu_status_t hstu_attn_bwd(const hstu_params_t* params, int32_t batch, const in
   if (!mark(0)) return HSTU_ERR_LAUNCH;
   if (!empty) {
     if (launch_sched(s, stream) != hipSuccess) return HSTU_ERR_LAUNCH;
-    if (launch_attn(a, params->dtype, params->head_dim, MODE_FULL, s.max_items, stream) != hipSuccess)
+    if (!saved && launch_attn(a, params->dtype, params->head_dim, MODE_FULL, s.max_items, stream) != hipSuccess)
       return HSTU_ERR_LAUNCH;
   }
   // 2. norm + gating backward: dU, dO, affine gradients
   LnBwdArgs l = {};
   l.o = (const float*)((char*)ws + w.o_off);
+  if (saved) {  // the norm-ready store's layout (see norm_ready)
+    l.o_dev = (const bf16*)((char*)ws + w.o_off);
+    l.o_stats = (const float*)((char*)ws + w.o_off + (size_t)total_tokens * (size_t)HD * 2);
+    l.head_dim = params->head_dim;
+  }
   l.u = u;
   l.dy = dy;
   l.ln_w = params->ln_w;

@@ -192,6 +192,11 @@ struct RabReduceArgs {
 // (bf16), plus per-wave partial sums of the affine gradients.
 struct LnBwdArgs {
   const float* o;                // [T, HD] attention output before the norm
+  // or, when o_dev is set, the forward's norm-ready store: bf16 deviations
+  // from each head's mean [T, HD] and per-head (mean, M2) [T, H]
+  const bf16* o_dev;
+  const float* o_stats;
+  int32_t head_dim;
   const void* u;
   const void* dy;
   const float* ln_w;

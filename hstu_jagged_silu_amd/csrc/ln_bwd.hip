@@ -12,8 +12,8 @@
 // are added in wave order through LDS and written once as the workgroup's
 // partial. A second kernel adds the partials in a fixed order, so the result
 // does not depend on timing.
-// HBM-bound: per element it reads O (4 B), U and dY (2 B each) and writes dU
-// and dO (2 B each).
+// HBM-bound: per element it reads O (4 B; 2 B of deviations from the saved
+// forward), U and dY (2 B each) and writes dU and dO (2 B each).
 #include "kernels.h"
 
 namespace hstu {
@@ -36,8 +36,12 @@ __device__ inline void st_bf4(bf16* p, f32x4 x) {
   *(bf16x4*)p = v;
 }
 
-// NCH: 4-element chunks per lane (see ln_gate_kernel)
-template <int NCH, bool FULL_LANES>
+// NCH: 4-element chunks per lane (see ln_gate_kernel). DEV: the input is the
+// forward's norm-ready store instead of fp32 O: the row's mean and variance
+// come from the heads' (mean, M2) pairs (merged as in the forward's norm,
+// mean = average of mean_h, M2 = sum M2_h + d sum (mean_h - mean)^2), and
+// o - mean = deviation + (mean_h - mean).
+template <int NCH, bool FULL_LANES, bool DEV>
 __global__ __launch_bounds__(64 * LNB_WAVES) void ln_bwd_kernel(LnBwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -58,32 +62,58 @@ __global__ __launch_bounds__(64 * LNB_WAVES) void ln_bwd_kernel(LnBwdArgs a) {
   const float inv_hd = 1.0f / (float)a.HD;
   const int64_t row_end = min<int64_t>(a.T, (int64_t)(blockIdx.x + 1) * a.rows_per_block);
   for (int64_t row = (int64_t)blockIdx.x * a.rows_per_block + wave; row < row_end; row += LNB_WAVES) {
-    const float* orow = a.o + row * a.HD;
     const bf16* urow = (const bf16*)a.u + row * a.HD;
     const bf16* yrow = (const bf16*)a.dy + row * a.HD;
     f32x4 z[NCH], u[NCH], g[NCH];
-    #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      z[i] = *(const f32x4*)(orow + col[i]);
-      u[i] = ld_bf4(urow + col[i]);
-      g[i] = ld_bf4(yrow + col[i]);  // dy for now
-    }
-    float s = 0.0f;
-    #pragma unroll
-    for (int i = 0; i < NCH; ++i)
-      if (on[i]) s += (z[i][0] + z[i][1]) + (z[i][2] + z[i][3]);
-    const float mean = lnb_wave_sum(s) * inv_hd;
-    float ss = 0.0f;
-    #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      if (!on[i]) continue;
+    float rstd;
+    if constexpr (DEV) {
+      const int H = a.HD / a.head_dim;
+      const bf16* drow = a.o_dev + row * a.HD;
+      const float* srow = a.o_stats + 2 * row * H;
+      float mh[NCH];
       #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        z[i][e] -= mean;
-        ss = fmaf(z[i][e], z[i][e], ss);
+      for (int i = 0; i < NCH; ++i) {
+        z[i] = ld_bf4(drow + col[i]);
+        u[i] = ld_bf4(urow + col[i]);
+        g[i] = ld_bf4(yrow + col[i]);  // dy for now
+        mh[i] = srow[2 * (col[i] / a.head_dim)];
       }
+      const f32x2 st = lane < H ? *(const f32x2*)(srow + 2 * lane) : f32x2{0.0f, 0.0f};
+      const float mean = lnb_wave_sum(st[0]) / (float)H;
+      const float dm = lane < H ? st[0] - mean : 0.0f;
+      const float m2 = lnb_wave_sum(fmaf((float)a.head_dim * dm, dm, st[1]));
+      rstd = rsqrtf(m2 * inv_hd + a.eps);
+      #pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const float shift = mh[i] - mean;
+        #pragma unroll
+        for (int e = 0; e < 4; ++e) z[i][e] += shift;
+      }
+    } else {
+      const float* orow = a.o + row * a.HD;
+      #pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        z[i] = *(const f32x4*)(orow + col[i]);
+        u[i] = ld_bf4(urow + col[i]);
+        g[i] = ld_bf4(yrow + col[i]);  // dy for now
+      }
+      float s = 0.0f;
+      #pragma unroll
+      for (int i = 0; i < NCH; ++i)
+        if (on[i]) s += (z[i][0] + z[i][1]) + (z[i][2] + z[i][3]);
+      const float mean = lnb_wave_sum(s) * inv_hd;
+      float ss = 0.0f;
+      #pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        if (!on[i]) continue;
+        #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          z[i][e] -= mean;
+          ss = fmaf(z[i][e], z[i][e], ss);
+        }
+      }
+      rstd = rsqrtf(lnb_wave_sum(ss) * inv_hd + a.eps);
     }
-    const float rstd = rsqrtf(lnb_wave_sum(ss) * inv_hd + a.eps);
     bf16* durow = (bf16*)a.du + row * a.HD;
     float s1 = 0.0f, s2 = 0.0f;
     #pragma unroll
@@ -190,6 +220,21 @@ __global__ __launch_bounds__(64 * RED_GROUPS) void ln_affine_reduce_kernel(LnBwd
   }
 }
 
+template <bool DEV>
+static void launch_ln_bwd_rows(const LnBwdArgs& a, dim3 grid, dim3 blk, hipStream_t s) {
+  switch (a.HD) {
+    case 256: hipLaunchKernelGGL((ln_bwd_kernel<1, true, DEV>), grid, blk, 0, s, a); return;
+    case 512: hipLaunchKernelGGL((ln_bwd_kernel<2, true, DEV>), grid, blk, 0, s, a); return;
+    case 1024: hipLaunchKernelGGL((ln_bwd_kernel<4, true, DEV>), grid, blk, 0, s, a); return;
+    case 2048: hipLaunchKernelGGL((ln_bwd_kernel<8, true, DEV>), grid, blk, 0, s, a); return;
+  }
+  const int nch = (int)ceil_div(a.HD / 4, 64);
+  if (nch <= 1) hipLaunchKernelGGL((ln_bwd_kernel<1, false, DEV>), grid, blk, 0, s, a);
+  else if (nch <= 2) hipLaunchKernelGGL((ln_bwd_kernel<2, false, DEV>), grid, blk, 0, s, a);
+  else if (nch <= 4) hipLaunchKernelGGL((ln_bwd_kernel<4, false, DEV>), grid, blk, 0, s, a);
+  else hipLaunchKernelGGL((ln_bwd_kernel<8, false, DEV>), grid, blk, 0, s, a);
+}
+
 hipError_t launch_ln_bwd(const LnBwdArgs& a, hipStream_t s) {
   if (a.HD <= 0) return hipSuccess;
   if (a.T <= 0 || a.nwaves <= 0) {  // no rows: the affine gradients are zero
@@ -198,18 +243,12 @@ hipError_t launch_ln_bwd(const LnBwdArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   const dim3 grid((unsigned)a.nwaves), blk(64 * LNB_WAVES);
-  switch (a.HD) {
-    case 256: hipLaunchKernelGGL((ln_bwd_kernel<1, true>), grid, blk, 0, s, a); break;
-    case 512: hipLaunchKernelGGL((ln_bwd_kernel<2, true>), grid, blk, 0, s, a); break;
-    case 1024: hipLaunchKernelGGL((ln_bwd_kernel<4, true>), grid, blk, 0, s, a); break;
-    case 2048: hipLaunchKernelGGL((ln_bwd_kernel<8, true>), grid, blk, 0, s, a); break;
-    default: {
-      const int nch = (int)ceil_div(a.HD / 4, 64);
-      if (nch <= 1) hipLaunchKernelGGL((ln_bwd_kernel<1, false>), grid, blk, 0, s, a);
-      else if (nch <= 2) hipLaunchKernelGGL((ln_bwd_kernel<2, false>), grid, blk, 0, s, a);
-      else if (nch <= 4) hipLaunchKernelGGL((ln_bwd_kernel<4, false>), grid, blk, 0, s, a);
-      else hipLaunchKernelGGL((ln_bwd_kernel<8, false>), grid, blk, 0, s, a);
-    }
+  if (a.o_dev != nullptr) {
+    if (a.head_dim < 4 || a.head_dim % 4 != 0 || a.HD % a.head_dim != 0 || a.HD / a.head_dim > 64)
+      return hipErrorInvalidValue;
+    launch_ln_bwd_rows<true>(a, grid, blk, s);
+  } else {
+    launch_ln_bwd_rows<false>(a, grid, blk, s);
   }
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   if (a.d_ln_w || a.d_ln_b)

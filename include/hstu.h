@@ -134,7 +134,8 @@ typedef enum {
  *                 makes an fp32 round trip instead (twice the bytes); the two
  *                 agree within bf16 rounding of the deviations. fp32 layers,
  *                 the split paged paths and the backward always use fp32.
- *                 Other bits: HSTU_ERR_INVALID_ARG.
+ *                 HSTU_FLAG_SAVED_FORWARD (read by hstu_attn_bwd only): see
+ *                 hstu_attn_bwd. Other bits: HSTU_ERR_INVALID_ARG.
  */
 typedef struct {
   int32_t num_heads;
@@ -157,6 +158,7 @@ typedef struct {
 
 /* hstu_params_t.flags bits */
 #define HSTU_FLAG_FP32_NORM_INPUT 1
+#define HSTU_FLAG_SAVED_FORWARD 2
 
 /*
  * Paged KV cache ("paged GPU table", page "recomendador-generativo-hstu-
@@ -260,6 +262,16 @@ typedef struct {
  * scheduling: every sum runs in a fixed order. params->timing_events, if
  * set, are recorded [0] before the recomputed forward, [1] before the norm
  * backward, [2] before the attention backward, [3] at the end.
+ * Saved forward (params->flags & HSTU_FLAG_SAVED_FORWARD): ws must be the
+ * workspace that an hstu_attn_fwd call with the same params (bar this bit),
+ * batch, seq_offsets, max_len, total_tokens and q, k, v, u, ts used last,
+ * unchanged since (a workspace sized for the backward also serves the
+ * forward). That call left its norm-ready attention store there (per token
+ * and head the mean and sum of squared deviations, and the bf16 deviations);
+ * the backward then does not recompute the attention forward and takes the
+ * norm backward's input from it. With HSTU_FLAG_FP32_NORM_INPUT also set:
+ * HSTU_ERR_INVALID_ARG. Anything else in ws leaves the gradients
+ * unspecified (no memory outside the given buffers is touched).
  */
 hstu_status_t hstu_attn_bwd(const hstu_params_t* params, int32_t batch, const int32_t* seq_offsets,
                             int32_t max_len, int64_t total_tokens, const void* q, const void* k,

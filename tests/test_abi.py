@@ -127,7 +127,8 @@ def test_workspace_size_valid_and_invalid():
     assert _ws(0, p, -1, 1024, 128) == 0
     assert _ws(0, _params(ln_eps=0.0), 8, 1024, 128) == 0
     assert _ws(0, _params(flags=hs.HSTU_FLAG_FP32_NORM_INPUT), 8, 65536, 8192) == full  # same workspace
-    assert _ws(0, _params(flags=2), 8, 1024, 128) == 0          # unknown flag bit
+    assert _ws(0, _params(flags=hs.HSTU_FLAG_SAVED_FORWARD), 8, 65536, 8192) == full  # same workspace
+    assert _ws(0, _params(flags=4), 8, 1024, 128) == 0          # unknown flag bit
 
 
 FAKE = 0x10000  # aligned, never dereferenced: validation fails before any launch
@@ -297,7 +298,10 @@ def test_backward_workspace_and_bad_arguments_before_launch():
     assert call(q=None, wsb=1 << 40) == INVALID
     assert call(q=FAKE + 4, wsb=1 << 40) == INVALID
     assert call(p=_params(head_dim=48)) == UNSUPPORTED
+    both = hs.HSTU_FLAG_SAVED_FORWARD | hs.HSTU_FLAG_FP32_NORM_INPUT
+    assert call(p=_params(flags=both), wsb=1 << 40) == INVALID  # a saved forward has no fp32 store
     assert call(B=0, wsb=1 << 40) == OK      # nothing to compute and no table or affine gradient requested
+    assert call(p=_params(flags=hs.HSTU_FLAG_SAVED_FORWARD), B=0, wsb=1 << 40) == OK
 
 
 def test_matmul_rejects_bad_arguments_before_launch():

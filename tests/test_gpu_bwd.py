@@ -46,6 +46,29 @@ def run_bwd(inp, dy, per_head_tables=False, affine=None, alpha=1.0, norm_n=0, ta
     return g, ref
 
 
+def run_bwd_saved(inp, dy, affine=None):
+    """Forward, then the backward on the forward's workspace with
+    HSTU_FLAG_SAVED_FORWARD (no recomputed forward; the norm backward reads
+    the forward's norm-ready store)."""
+    H, d = inp.num_heads, inp.head_dim
+    ln_w, ln_b = affine if affine is not None else (None, None)
+    p = hs.LayerParams(num_heads=H, head_dim=d, dtype=BF, pos_tab=dev(inp.tables.pos), time_tab=dev(inp.tables.time),
+                       ln_w=None if ln_w is None else dev(ln_w), ln_b=None if ln_b is None else dev(ln_b),
+                       flags=hs.HSTU_FLAG_SAVED_FORWARD)
+    B, T, L = len(inp.seq_offsets) - 1, inp.total, max(1, inp.max_len)
+    ws = torch.empty(hs.hstu_workspace_size(hs.HSTU_FN_FULL_BWD, p, B, T, L), dtype=torch.uint8, device="cuda")
+    q, k, v, u, ts, off = (dev(inp.q, BF), dev(inp.k, BF), dev(inp.v, BF), dev(inp.u, BF), dev(inp.ts),
+                           dev(inp.seq_offsets))
+    y = hs.hstu_attn_fwd(q, k, v, u, ts, off, L, p, workspace=ws)
+    dy_d = dev(dy, BF)
+    g = hs.hstu_attn_bwd(q, k, v, u, ts, off, L, dy_d, p, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.hstu_full_bwd(inp.q, inp.k, inp.v, inp.u, inp.ts, inp.seq_offsets, dy, inp.tables.pos,
+                               inp.tables.time, 1.0, 0, ln_w, ln_b, magnitudes=True)
+    again = lambda: hs.hstu_attn_bwd(q, k, v, u, ts, off, L, dy_d, p, workspace=ws)
+    return y, g, ref, again
+
+
 def check(g, ref, label=""):
     errs, bars = {}, {}
     for name, rname in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("du", "du"), ("d_pos_tab", "dpos"),
@@ -164,3 +187,26 @@ def test_single_token_users_and_empty_batch():
     torch.cuda.synchronize()
     for k in ("d_pos_tab", "d_time_tab", "d_ln_w", "d_ln_b"):
         assert not torch.any(out[k]), k
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_saved_forward_all_gradients(d):
+    """The backward on the forward's workspace (HSTU_FLAG_SAVED_FORWARD): the
+    norm backward takes the forward's bf16 deviations and per-head statistics
+    instead of a recomputed fp32 output; every gradient against the oracle,
+    and a second backward call on the same workspace gives the same bits."""
+    inp = W.jagged(f"bwd_saved_d{d}", 71, [1, 77, 200, 130, 0, 64, 129], 2, d, "bf16", 128, 128)
+    dy = W.upstream_grad(72, inp.u.shape)
+    _, g, ref, again = run_bwd_saved(inp, dy, affine=W.affine_terms(73, 2 * d))
+    check(g, ref, label=f"saved forward d={d}")
+    g2 = again()
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv", "du", "d_pos_tab", "d_time_tab", "d_ln_w", "d_ln_b"):
+        assert torch.equal(g[name], g2[name]), name
+
+
+def test_saved_forward_training_shape():
+    inp = W.training_shape()
+    dy = W.upstream_grad(69, inp.u.shape)
+    _, g, ref, _ = run_bwd_saved(inp, dy, affine=W.affine_terms(70, 512))
+    check(g, ref, label="saved forward, training shape")
