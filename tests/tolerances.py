@@ -12,6 +12,9 @@ errors of spread u / sqrt(3) each give an error of spread at most
 sigma = u sqrt(4 / 3) R, about 1.15 u R, whatever the signs of the terms.
 Over at most 10^7 entries a Gaussian stays below 5.7 sigma; the bar 8 u is
 about 7 sigma (a false alarm about once in 3 * 10^4 runs of 10^7 entries).
+The backward on the forward's saved output (HSTU_FLAG_SAVED_FORWARD) adds
+one rounding, the forward's bf16 deviations behind dO: five roundings,
+sigma = u sqrt(5 / 3), about 1.29 u R, and the bar is about 6.2 sigma.
 A term that is missing altogether costs about its own size; on random data
 one 64-key tile of a row is a large part of R (a CPU pin shows such a dQ
 scoring far above the bar).
