@@ -1328,6 +1328,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_ds_kernel(BwdArgs a) 
       for (int db = 0; db < G::NDB; ++db) dqacc[db] = Mfma<T>::run(kt[ks & 1][db], dsb[ks], dqacc[db]);
     }
     if (!has_pos && !has_time) return;
+    // dsb[ks] for a key step held in a scalar register (selects, no dynamic
+    // register indexing): element j is dS of key 16 ks + 8 hl + j and this
+    // lane's query, the same bf16 value the block in LDS holds
+    auto dsb_step = [&](int ks) { return ks == 0 ? dsb[0] : ks == 1 ? dsb[1] : ks == 2 ? dsb[2] : dsb[3]; };
     // Bias-table histograms. A sum over a set of pairs is an MFMA of their
     // dS^T operands against a ones operand (every row of the result holds the
     // per-query sums; lane l < 32 has query l). Tiles whose pairs all share
@@ -1389,7 +1393,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_ds_kernel(BwdArgs a) 
       // a time (a rolled loop keeps the selects from holding many masks)
       #pragma unroll 1
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 d = ks == 0 ? dsb[0] : ks == 1 ? dsb[1] : ks == 2 ? dsb[2] : dsb[3];
+        const bf16x8 d = dsb_step(ks);
         #pragma unroll
         for (int j = 0; j < 8; ++j) pos_far += lim_rel - 16 * ks - j >= n_pos - 1 ? (float)d[j] : 0.0f;
       }
@@ -1419,24 +1423,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_ds_kernel(BwdArgs a) 
       #pragma unroll
       for (int i = 0; i < NB; ++i) bound[i] = -(int32_t)(((uint32_t)2 << (b_lo + i)) - 1u);
       float tot = 0.0f, ge[NB > 0 ? NB : 1] = {};
-      // dS read back from the block in LDS, 8 pairs at a time (holding all
-      // 32 converted values at once would cost registers the kernel lacks)
-      LB* blk = dl + (wave >> 1) * DS_BLOCK * 2;
-      const int col = (wave & 1) * 32 + (lane & 31);
+      // the pairs' dS are this lane's MFMA operands (dsb), 8 pairs at a time
       #pragma unroll 1
       for (int ks = 0; ks < 4; ++ks) {
-        uint32_t ad[8], at[8], vd[8], vt[8];
+        uint32_t at[8], vt[8];
         #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int kk = 16 * ks + 8 * hl + j;
-          ad[j] = (uint32_t)(uintptr_t)blk + ds_chunk_off(kk, col >> 3) + (col & 7) * 2;
-          at[j] = (uint32_t)(uintptr_t)(tsl_lo + 16 * ks + j);
-        }
-        lds_read8_u16(ad, vd);
+        for (int j = 0; j < 8; ++j) at[j] = (uint32_t)(uintptr_t)(tsl_lo + 16 * ks + j);
         lds_read8_b32(at, vt);
+        const bf16x8 d = dsb_step(ks);
         #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float ds = bf16_bits_to_f32(vd[j]);
+          const float ds = (float)d[j];
           const int32_t dk = (int32_t)vt[j] - tsq_lo;
           tot += ds;
           #pragma unroll
@@ -1461,26 +1458,23 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_ds_kernel(BwdArgs a) 
       const int b_top = min(63 - __builtin_clzll((uint64_t)max(span, (int64_t)0) + 1), n_time_eff - 1);
       win_fit(max(0, b_top - 7), b_top);
     }
-    // (a rolled loop over the lane's 32 pairs, 8 at a time, reading dS back
-    // from the block in LDS: this path is rare, and unrolled selects would
-    // hold too many lane masks)
+    // (a rolled loop over the lane's 32 pairs, 8 at a time, their dS taken
+    // from this lane's MFMA operands: this path is rare, and unrolled
+    // selects would hold too many lane masks)
     auto per_pair = [&](auto small_tag) {
       constexpr bool SMALL = decltype(small_tag)::value;
-      LB* blk = dl + (wave >> 1) * DS_BLOCK * 2;
-      const int col = (wave & 1) * 32 + (lane & 31);  // this lane's query in the block
       const uint32_t t_lo = (uint32_t)(uintptr_t)LDS_PTR(const int32_t, st.ts_lo);
       const uint32_t t64 = (uint32_t)(uintptr_t)LDS_PTR(const int64_t, st.ts64);
       // pairs e0 .. e0 + 7 of the lane (keys 16 (e / 8) + 8 hl + e mod 8): dS and bucket
       auto pairs8 = [&](int e0, float (&ds)[8], int (&bkt)[8]) {
-        uint32_t ad[8], at[8], vd[8], vt[8], vh[8];
+        uint32_t at[8], vt[8], vh[8];
         #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int kk = 16 * (e0 >> 3) + 8 * hl + e;
-          ad[e] = (uint32_t)(uintptr_t)blk + ds_chunk_off(kk, col >> 3) + (col & 7) * 2;
           at[e] = SMALL ? t_lo + 4 * kk : t64 + 8 * kk;
         }
-        lds_read8_u16(ad, vd);
         lds_read8_b32(at, vt);
+        const bf16x8 d = dsb_step(e0 >> 3);
         if constexpr (!SMALL) {
           #pragma unroll
           for (int e = 0; e < 8; ++e) at[e] += 4;
@@ -1488,7 +1482,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_ds_kernel(BwdArgs a) 
         }
         #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          ds[e] = bf16_bits_to_f32(vd[e]);
+          ds[e] = (float)d[e];
           const int64_t tk = SMALL ? 0 : (int64_t)(((uint64_t)vh[e] << 32) | vt[e]);
           bkt[e] = min(63 - time_z<SMALL>(tsq, tk, tsq_lo, (int32_t)vt[e]), n_time_eff - 1);
         }
