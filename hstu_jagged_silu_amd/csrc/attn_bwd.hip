@@ -1452,7 +1452,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_ds_kernel(BwdArgs a) 
     if (nb == 4) { by_threshold(std::integral_constant<int, 3>{}); return; }
     // Pair by pair: the window is placed on the tile's highest possible
     // bucket, so no pair lies above it; pairs below it (only where keys come
-    // very close in time to a query) are summed bucket by bucket
+    // very close in time to a query) are summed by further passes, eight
+    // buckets at a time
     {
       const int64_t span = max(w_ts_max - kmin, kmax - w_ts_min);
       const int b_top = min(63 - __builtin_clzll((uint64_t)max(span, (int64_t)0) + 1), n_time_eff - 1);
@@ -1496,22 +1497,28 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_ds_kernel(BwdArgs a) 
         #pragma unroll
         for (int e = 0; e < 8; ++e) {
           win_add(bkt[e], ds[e]);
-          b_below = bkt[e] < wb ? min(b_below, bkt[e]) : b_below;
+          // masked pairs (dS exactly 0, often with a small |dt|) add nothing
+          b_below = (bkt[e] < wb && ds[e] != 0.0f) ? min(b_below, bkt[e]) : b_below;
         }
       }
       for (int m = 32; m >= 1; m >>= 1) b_below = min(b_below, __shfl_xor(b_below, m));
-      for (int b = b_below; b < wb; ++b) {  // wave-uniform, usually empty
-        float x = 0.0f;
+      // buckets [b_below, wb): the window moves down to the eight buckets
+      // under the last ones counted (after a flush), and a pass adds the
+      // pairs below those only; wave-uniform, usually one pass at most
+      int top = wb;
+      while (b_below < top) {
+        const int base = max(b_below, top - 8);
+        flush_win();
+        wb = base;
         #pragma unroll 1
         for (int e0 = 0; e0 < 32; e0 += 8) {
           float ds[8];
           int bkt[8];
           pairs8(e0, ds, bkt);
           #pragma unroll
-          for (int e = 0; e < 8; ++e) x += bkt[e] == b ? ds[e] : 0.0f;
+          for (int e = 0; e < 8; ++e) win_add(bkt[e], bkt[e] < top ? ds[e] : 0.0f);
         }
-        x = wave_sum_f(x);
-        if (lane == 0) lds_add_f32_unordered(&hist.time[wave][b], x);
+        top = base;
       }
     };
     if (small_span) per_pair(std::true_type{});
