@@ -1275,13 +1275,31 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_bwd_dq_ds_kernel(BwdArgs a) 
   #pragma unroll
   for (int s = 0; s < 8; ++s) win[s] = 0.0f;
   int wb = 0;
+  // The eight slot sums over the wave by recursive halving: across lane bit
+  // 5, then 4, then 3, a lane keeps half of its slots and adds its partner's
+  // copies of them (4 + 2 + 1 shuffles), then a plain sum over lane bits 2..0
+  // (3 more), instead of eight separate six-shuffle wave sums. Lane l ends
+  // with slot 4 b5 + 2 b4 + b3 of its bits; lanes 8s add slot s.
   auto flush_win = [&]() {
+    const bool b5 = (lane & 32) != 0, b4 = (lane & 16) != 0, b3 = (lane & 8) != 0;
+    // in place: after each level win[0 ..) holds the lane's remaining slots
     #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const float x = wave_sum_f(win[s]);
-      if (lane == 0 && wb + s < 64) lds_add_f32_unordered(&hist.time[wave][wb + s], x);
-      win[s] = 0.0f;
+    for (int j = 0; j < 4; ++j) {
+      const float send = b5 ? win[j] : win[j + 4], keep = b5 ? win[j + 4] : win[j];
+      win[j] = keep + __shfl_xor(send, 32);
     }
+    #pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float send = b4 ? win[j] : win[j + 2], keep = b4 ? win[j + 2] : win[j];
+      win[j] = keep + __shfl_xor(send, 16);
+    }
+    float x = (b3 ? win[1] : win[0]) + __shfl_xor(b3 ? win[0] : win[1], 8);
+    #pragma unroll
+    for (int m = 4; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    const int slot = (b5 ? 4 : 0) + (b4 ? 2 : 0) + (b3 ? 1 : 0);
+    if ((lane & 7) == 0 && wb + slot < 64) lds_add_f32_unordered(&hist.time[wave][wb + slot], x);
+    #pragma unroll
+    for (int j = 0; j < 8; ++j) win[j] = 0.0f;
   };
   // make buckets [lo, hi] (hi - lo < 8, wave-uniform) fit the window
   auto win_fit = [&](int lo, int hi) {
