@@ -199,12 +199,15 @@ __device__ inline uint32_t tr_off_b(int lane, int db, int c, int s4) {
   return (uint32_t)(b_off<D>(row, d / G::EPC) + (d % G::EPC) * 2);
 }
 
-// y -> (P', dS') for one score: P' = y * sigma, dS' = dp * sigma * (1 + x (1 - sigma)), x = -ln2 y
+// y -> (P', dS') for one score: P' = y * sigma, dS' = dp * sigma * (1 + x (1 - sigma)), x = -ln2 y.
+// Since x sigma = -ln2 P', the last factor is 1 - ln2 y + ln2 P': two fma
+// instead of a multiply, a subtract and an fma (both forms carry an absolute
+// error of order |x| 2^-24 in that factor)
 __device__ inline void silu_fwd_bwd(float y, float dp, float& p, float& ds) {
   const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
   p = y * sg;
-  const float x = -LN2 * y;
-  ds = dp * sg * fmaf(x, 1.0f - sg, 1.0f);
+  const float w = fmaf(LN2, p, fmaf(-LN2, y, 1.0f));
+  ds = (dp * sg) * w;
 }
 
 // Stage HBM -> LDS of KT rows of two [T, H, D] tensors (rows r0 .. r0 + KT - 1
